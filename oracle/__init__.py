@@ -1,0 +1,113 @@
+"""CPU oracle for C = A x B with int8 inputs and int32 results.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything here.  The
+product library never links, loads or calls it, and nothing here imports the
+product package: the two share no code.
+
+Contents
+  * ``oracle.c`` (built with gcc into ``liboracle.so``): the plain triple loop
+    over the definition C[i][j] = wrap32(sum_k A[i][k] * B[k][j]) with an exact
+    int64 sum, for row-major A and row- or column-major B.
+  * ``selector.py``: the tile-configuration selection method of patent
+    application CN114238853A (claims 1-6), written as plain Python from the
+    claims' steps, with the readings of the steps whose formulas are missing
+    from the text.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP).  Returns the library path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                        "-o", tmp, _SRC], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_gemm_s8s8s32.restype = i64
+        lib.oracle_gemm_s8s8s32.argtypes = [i64, i64, i64, p, i64, p, i64, ctypes.c_int, p, i64]
+        lib.oracle_gemm_element.restype = ctypes.c_int32
+        lib.oracle_gemm_element.argtypes = [i64, i64, i64, p, i64, p, i64, ctypes.c_int]
+        lib.oracle_gemm_elements.restype = None
+        lib.oracle_gemm_elements.argtypes = [i64, p, p, i64, p, i64, p, i64, ctypes.c_int, p]
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def _check_storage(A, B, M, N, K, b_col_major):
+    assert A.dtype == np.int8 and B.dtype == np.int8
+    assert A.ndim == 2 and B.ndim == 2 and A.strides[1] == 1 and B.strides[1] == 1
+    assert A.shape[0] >= M and A.shape[1] >= K
+    if b_col_major:
+        assert B.shape[0] >= N and B.shape[1] >= K
+    else:
+        assert B.shape[0] >= K and B.shape[1] >= N
+
+
+def gemm(A: np.ndarray, B: np.ndarray, b_col_major: bool, M=None, N=None, K=None,
+         C: np.ndarray | None = None, return_overflow: bool = False):
+    """C = A x B from storage arrays.
+
+    A: 2-D int8, row-major, shape (>=M, lda) with lda >= K (its row stride is lda).
+    B: row-major K x N storage (b_col_major False) or N x K storage (True).
+    Sizes default to the tight ones implied by the shapes.  Returns an (M, N)
+    int32 array (or writes into C, whose rows may be padded).
+    """
+    if M is None:
+        M = A.shape[0]
+    if K is None:
+        K = A.shape[1]
+    if N is None:
+        N = B.shape[0] if b_col_major else B.shape[1]
+    _check_storage(A, B, M, N, K, b_col_major)
+    if C is None:
+        C = np.zeros((M, N), dtype=np.int32)
+    assert C.dtype == np.int32 and C.strides[1] == 4 and C.shape[0] >= M and C.shape[1] >= N
+    lda, ldb, ldc = A.strides[0], B.strides[0], C.strides[0] // 4
+    ovf = _load().oracle_gemm_s8s8s32(M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb,
+                                      1 if b_col_major else 0, C.ctypes.data, ldc)
+    return (C, int(ovf)) if return_overflow else C
+
+
+def gemm_elements(A: np.ndarray, B: np.ndarray, b_col_major: bool, K: int,
+                  rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """C[rows[t], cols[t]] for each t, by the same definition."""
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    assert rows.shape == cols.shape
+    out = np.empty(rows.shape, dtype=np.int32)
+    _load().oracle_gemm_elements(rows.size, rows.ctypes.data, cols.ctypes.data, K,
+                                 A.ctypes.data, A.strides[0], B.ctypes.data, B.strides[0],
+                                 1 if b_col_major else 0, out.ctypes.data)
+    return out
+
+
+def gemm_element(A, B, b_col_major, K, i, j) -> int:
+    return int(_load().oracle_gemm_element(i, j, K, A.ctypes.data, A.strides[0],
+                                           B.ctypes.data, B.strides[0], 1 if b_col_major else 0))

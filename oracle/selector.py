@@ -1,0 +1,183 @@
+"""Tile-configuration selection of patent application CN114238853A, in plain Python.
+
+TEST INFRASTRUCTURE (see the package docstring): the product's C++ selector is
+checked against this function; neither imports the other.
+
+Source: "一种矩阵乘分片配置选择方法及系统" (method and system for selecting a
+matrix-multiply tiling configuration), claims 1 to 7.  Claim 1 gives five
+steps; claims 2-6 refine steps 2-5, but their formulas were images and are
+missing from the text, so the readings below fill them in.  Each is listed in
+the design notes.
+
+A configuration (one compiled kernel) is described by:
+  family          'general' or 'skinny'
+  mfma_m, mfma_n  M and N extent of one matrix-core instruction tile
+  waves_m, waves_n  waves of the thread block along M and N
+  m_tiles, n_tiles  per-wave repeats along M and N (the claims' data reuse counts)
+  block_k         K extent of one K-tile (the claims' block_k_threads)
+  threads         threads per block
+  blocks_per_cu   blocks of this kernel resident on one compute unit at once
+                  (claim 6's block_per_cu; on the device it comes from the
+                  runtime occupancy query, which applies the register, LDS and
+                  wave-slot limits)
+Derived: block_m_threads = waves_m * mfma_m, block_n_threads = waves_n * mfma_n,
+the block tile BM = block_m_threads * m_tiles and BN = block_n_threads * n_tiles.
+
+Hardware description: num_cu, max_threads_per_block, min_active_threads
+(claim 3's threshold), skinny_max_m (the largest M sent to the skinny family).
+
+Readings:
+  claim 2 (TCU case): block_m_threads and block_n_threads are multiples of the
+      instruction's M and N extents, each at least the smallest instruction
+      extent (16), and the block has at most max_threads_per_block threads.
+  claim 3: a configuration survives step 2 if blocks_per_cu * threads, the
+      register-limited number of active threads on a compute unit, is at least
+      min_active_threads (one wave per SIMD: 4 * 64 on CDNA4).
+  claim 4: min_theory_block_num = num_cu * blocks_per_cu and
+      Thread_Blocks = ceil(m / BM) * ceil(n / BN).  A configuration survives if
+      Thread_Blocks >= min_theory_block_num; if none does, every step-2
+      survivor is replaced by its reuse-1 sibling (same thread split and
+      block_k, m_tiles = n_tiles = 1) and all are kept.
+  skinny route (CDNA4 addition): after that fallback, when m <= skinny_max_m,
+      the candidates are instead the skinny family with the smallest block
+      height BM >= m; those reaching Thread_Blocks >= num_cu are kept (all if
+      none), then steps 4 and 5 as below.
+  claim 5: the compute-to-memory ratio of a BM x BN tile over a K-tile of
+      depth BK is BM*BN*BK / (BM*BK + BK*BN) = BM*BN / (BM + BN) (the B tile's
+      width is read with n_tiles).  Step 4 keeps every configuration tied at
+      the maximum, compared exactly by cross-multiplication.
+  claim 6: Launch_kernel_times = ceil(Thread_Blocks / (num_cu * blocks_per_cu)),
+      the number of rounds of resident blocks.  Step 5 keeps the minimum.
+  Remaining ties: first in table order.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+@dataclass(frozen=True)
+class Hw:
+    num_cu: int = 256
+    max_threads_per_block: int = 1024
+    min_active_threads: int = 256
+    skinny_max_m: int = 32
+
+
+@dataclass(frozen=True)
+class Cfg:
+    id: int
+    family: str
+    mfma_m: int
+    mfma_n: int
+    waves_m: int
+    waves_n: int
+    m_tiles: int
+    n_tiles: int
+    block_k: int
+    threads: int
+    blocks_per_cu: int
+
+    @property
+    def block_m_threads(self) -> int:
+        return self.waves_m * self.mfma_m
+
+    @property
+    def block_n_threads(self) -> int:
+        return self.waves_n * self.mfma_n
+
+    @property
+    def BM(self) -> int:
+        return self.block_m_threads * self.m_tiles
+
+    @property
+    def BN(self) -> int:
+        return self.block_n_threads * self.n_tiles
+
+
+@dataclass
+class Result:
+    id: int
+    route: int                      # 0 general, 1 reuse-1 fallback, 2 skinny
+    trace: dict = field(default_factory=dict)
+
+
+def thread_blocks(c: Cfg, m: int, n: int) -> int:
+    return ceil_div(m, c.BM) * ceil_div(n, c.BN)
+
+
+def launch_times(c: Cfg, m: int, n: int, hw: Hw) -> int:
+    return ceil_div(thread_blocks(c, m, n), hw.num_cu * c.blocks_per_cu)
+
+
+def ratio_better(a: Cfg, b: Cfg) -> int:
+    """+1 if a's BM*BN/(BM+BN) is larger than b's, 0 if equal, -1 if smaller."""
+    lhs = a.BM * a.BN * (b.BM + b.BN)
+    rhs = b.BM * b.BN * (a.BM + a.BN)
+    return (lhs > rhs) - (lhs < rhs)
+
+
+def step2_ok(c: Cfg, hw: Hw) -> bool:
+    split_ok = (c.block_m_threads % c.mfma_m == 0 and c.block_n_threads % c.mfma_n == 0
+                and c.block_m_threads >= 16 and c.block_n_threads >= 16
+                and c.threads <= hw.max_threads_per_block)
+    return split_ok and c.blocks_per_cu >= 1 and c.blocks_per_cu * c.threads >= hw.min_active_threads
+
+
+def reuse1_sibling(c: Cfg, table: list[Cfg]) -> Cfg | None:
+    for d in table:
+        if (d.family == c.family and d.mfma_m == c.mfma_m and d.mfma_n == c.mfma_n
+                and d.waves_m == c.waves_m and d.waves_n == c.waves_n
+                and d.block_k == c.block_k and d.m_tiles == 1 and d.n_tiles == 1):
+            return d
+    return None
+
+
+def _steps_4_5(cands: list[Cfg], m: int, n: int, hw: Hw, trace: dict) -> Cfg:
+    best = cands[0]
+    for c in cands[1:]:
+        if ratio_better(c, best) > 0:
+            best = c
+    s4 = [c for c in cands if ratio_better(c, best) == 0]
+    trace["step4"] = [c.id for c in s4]
+    rounds = min(launch_times(c, m, n, hw) for c in s4)
+    s5 = [c for c in s4 if launch_times(c, m, n, hw) == rounds]
+    trace["step5"] = [c.id for c in s5]
+    return s5[0]
+
+
+def select(m: int, n: int, k: int, hw: Hw, table: list[Cfg]) -> Result:
+    """Pick a configuration id for an m x k times k x n product."""
+    trace: dict = {}
+    general = [c for c in table if c.family == "general"]
+    trace["step1"] = [c.id for c in general]
+    s2 = [c for c in general if step2_ok(c, hw)]
+    trace["step2"] = [c.id for c in s2]
+    if not s2:
+        raise ValueError("no configuration survives step 2")
+    s3 = [c for c in s2 if thread_blocks(c, m, n) >= hw.num_cu * c.blocks_per_cu]
+    route = 0
+    if not s3:
+        route = 1
+        seen, s3 = set(), []
+        for c in s2:
+            d = reuse1_sibling(c, table)
+            if d is not None and d.id not in seen and step2_ok(d, hw):
+                seen.add(d.id)
+                s3.append(d)
+        s3.sort(key=lambda c: c.id)
+        if m <= hw.skinny_max_m:
+            skinny = [c for c in table if c.family == "skinny" and c.BM >= m and step2_ok(c, hw)]
+            if skinny:
+                bm = min(c.BM for c in skinny)
+                skinny = [c for c in skinny if c.BM == bm]
+                route = 2
+                fill = [c for c in skinny if thread_blocks(c, m, n) >= hw.num_cu]
+                s3 = fill if fill else skinny
+    trace["step3"] = [c.id for c in s3]
+    trace["route"] = route
+    pick = _steps_4_5(s3, m, n, hw, trace)
+    return Result(pick.id, route, trace)

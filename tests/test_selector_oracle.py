@@ -1,0 +1,91 @@
+"""Pins for the Python reading of the patent's tile-configuration selector.
+
+The pages print no selector output, so against the pages this is "parity
+unpinned".  It is pinned instead by worked examples: each expected id below
+was derived by hand from the claims' rules on a small fake table, with the
+arithmetic written next to it."""
+import pytest
+
+from oracle.selector import Cfg, Hw, select, thread_blocks, launch_times, ratio_better
+
+
+def table(bpc4=2):
+    g = "general"
+    s = "skinny"
+    return [
+        Cfg(0, g, 32, 32, 2, 2, 4, 4, 128, 256, 1),   # 256 x 256
+        Cfg(1, g, 32, 32, 2, 2, 2, 2, 128, 256, 2),   # 128 x 128
+        Cfg(2, g, 32, 32, 2, 2, 1, 1, 128, 256, 4),   # 64 x 64, reuse-1 sibling of 0, 1, 3
+        Cfg(3, g, 32, 32, 2, 2, 2, 1, 128, 256, 2),   # 128 x 64
+        Cfg(4, g, 16, 16, 2, 2, 4, 4, 128, 256, bpc4),  # 128 x 128 with 16x16 tiles
+        Cfg(5, g, 16, 16, 2, 2, 1, 1, 128, 256, 8),   # 32 x 32, reuse-1 sibling of 4
+        Cfg(6, s, 16, 16, 1, 1, 1, 1, 64, 512, 2),    # skinny 16 x 16
+        Cfg(7, s, 16, 16, 1, 1, 1, 2, 64, 512, 2),    # skinny 16 x 32
+        Cfg(8, s, 16, 16, 1, 1, 2, 1, 64, 512, 2),    # skinny 32 x 16
+    ]
+
+
+HW = Hw(num_cu=256, max_threads_per_block=1024, min_active_threads=256, skinny_max_m=32)
+
+
+def test_derived_quantities():
+    t = table()
+    assert (t[0].BM, t[0].BN, t[3].BM, t[3].BN, t[8].BM, t[8].BN) == (256, 256, 128, 64, 32, 16)
+    assert thread_blocks(t[0], 4096, 4096) == 256
+    assert thread_blocks(t[3], 1000, 3000) == 8 * 47
+    assert launch_times(t[0], 16384, 16384, HW) == 16
+    assert ratio_better(t[0], t[1]) == 1 and ratio_better(t[1], t[4]) == 0 and ratio_better(t[3], t[1]) == -1
+
+
+@pytest.mark.parametrize("m,n,want_id,want_route", [
+    # 4096^2: every config fills (id0 256 >= 256*1, id1 1024 >= 512, ...); max ratio 256*256/512 = 128 -> id0
+    (4096, 4096, 0, 0),
+    # 16384^2: id0 has 4096 blocks, still the max ratio -> id0 (16 rounds)
+    (16384, 16384, 0, 0),
+    # 1000 x 3000: id0 48 < 256, id1 192 < 512, id2 752 < 1024, id3 376 < 512, id4 192 < 512,
+    # id5 32*94 = 3008 >= 2048 -> only id5 survives step 3
+    (1000, 3000, 5, 0),
+    # 256^2: nothing fills (id5 64 < 2048) -> reuse-1 siblings {2, 5}; ratio 32 > 16 -> id2, fallback
+    (256, 256, 2, 1),
+    # 16 x 4096: fallback, m <= 32 -> skinny with BM = 16: id6 has 256 blocks >= 256, id7 128 < 256 -> id6
+    (16, 4096, 6, 2),
+    # 16 x 8192: id6 512 and id7 256 both fill; ratio 16*32/48 > 16*16/32 -> id7
+    (16, 8192, 7, 2),
+    # 17 x 4096: smallest skinny BM >= 17 is 32 -> id8 (256 blocks)
+    (17, 4096, 8, 2),
+    # 33 x 4096: too tall for the skinny family -> fallback siblings {2, 5} -> id2
+    (33, 4096, 2, 1),
+    # 1 x 1: fallback then skinny; nothing fills, keep {6, 7}; ratio picks id7
+    (1, 1, 7, 2),
+])
+def test_worked_examples(m, n, want_id, want_route):
+    r = select(m, n, 4096, HW, table())
+    assert (r.id, r.route) == (want_id, want_route), r.trace
+
+
+def test_claim3_register_filter_and_step5_rounds():
+    hw = Hw(num_cu=256, max_threads_per_block=1024, min_active_threads=512, skinny_max_m=32)
+    # id0 has 1 * 256 = 256 < 512 active threads: dropped at step 2.
+    # 4096^2: best ratio 64 shared by id1 and id4; rounds ceil(1024 / 512) = 2 for both -> table order, id1
+    r = select(4096, 4096, 4096, hw, table())
+    assert 0 not in r.trace["step2"] and r.id == 1 and r.trace["step4"] == [1, 4]
+    # with id4 at 4 blocks per CU its rounds drop to ceil(1024 / 1024) = 1 -> id4
+    r = select(4096, 4096, 4096, hw, table(bpc4=4))
+    assert r.id == 4 and r.trace["step5"] == [4]
+
+
+def test_other_hardware():
+    # 304 compute units: id0 has 256 < 304 blocks at 4096^2 -> out; id1 and id4 tie on ratio 64
+    # and on rounds ceil(1024 / 608) = 2 -> id1
+    r = select(4096, 4096, 4096, Hw(num_cu=304), table())
+    assert r.id == 1 and r.route == 0
+    # 256-thread blocks only: the 512-thread skinny kernels are excluded, so 16 x 4096 stays
+    # on the reuse-1 fallback -> {2, 5} -> id2
+    r = select(16, 4096, 4096, Hw(max_threads_per_block=256), table())
+    assert (r.id, r.route) == (2, 1)
+
+
+def test_deterministic_and_k_independent():
+    a = [select(m, n, 64, HW, table()).id for m in (1, 16, 100, 4096) for n in (1, 300, 4096)]
+    b = [select(m, n, 8192, HW, table()).id for m in (1, 16, 100, 4096) for n in (1, 300, 4096)]
+    assert a == b
