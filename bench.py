@@ -1,0 +1,239 @@
+"""Throughput of the tiled int8 GEMM on one MI355X.
+
+One step = one call of the C-ABI entry point on device-resident inputs: host
+argument checks, tile-configuration selection and the kernel launch, i.e. the
+whole path.  The headline workload is the square M = N = K = 4096 product with
+row-major A and column-major B; the skinny M = 16, N = K = 4096 product (the
+HBM-bound half of the metric) is timed in the same run and reported under
+"skinny".  Inputs rotate over several buffer sets whose footprint exceeds the
+L2 and Infinity Cache, so every step reads A and B from HBM.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 matrix-core peak, 5.0 POP/s
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+MALL_BYTES = 256 << 20    # Infinity Cache
+
+WORKLOADS = {
+    "square4096": dict(M=4096, N=4096, K=4096, bcm=True,
+                       desc="int8 GEMM M=N=K=4096, A row-major, B column-major (N x K, K contiguous), C int32 row-major"),
+    "skinny16": dict(M=16, N=4096, K=4096, bcm=True,
+                     desc="int8 GEMM M=16, N=K=4096, A row-major, B column-major, C int32 row-major"),
+    "single256": dict(M=256, N=256, K=256, bcm=False,
+                      desc="int8 GEMM M=N=K=256, A and B row-major, C int32 row-major"),
+    "ragged": dict(M=1000, N=3000, K=777, bcm=True,
+                   desc="int8 GEMM M=1000, N=3000, K=777, A row-major, B column-major, C int32 row-major"),
+    "large16384": dict(M=16384, N=16384, K=8192, bcm=True,
+                       desc="int8 GEMM M=N=16384, K=8192, A row-major, B column-major, C int32 row-major"),
+}
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tiled_dense_int8_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def make_sets(w, nsets, seed=0):
+    import torch
+    import synthetic
+    A, B = synthetic.gemm_inputs(w["M"], w["N"], w["K"], seed)
+    Bs = synthetic.store_b(B, w["bcm"])
+    A_d = torch.from_numpy(A).cuda()
+    B_d = torch.from_numpy(Bs).cuda()
+    sets = []
+    for i in range(nsets):
+        a = A_d if i == 0 else A_d.clone()
+        b = B_d if i == 0 else B_d.clone()
+        c = torch.empty((w["M"], w["N"]), dtype=torch.int32, device="cuda")
+        sets.append((a, b, c))
+    return A, Bs, sets
+
+
+def rotation_sets(w):
+    per = w["M"] * w["K"] + w["K"] * w["N"] + 4 * w["M"] * w["N"]
+    return max(2, min(64, -(-3 * MALL_BYTES // per)))
+
+
+def time_workload(t, w, steps, warmup):
+    """(wall ms per step, kernel ms per launch by events, config id, sets)."""
+    import torch
+    nsets = rotation_sets(w)
+    A, Bs, sets = make_sets(w, nsets)
+    M, N, K = w["M"], w["N"], w["K"]
+    fn = t.gemm_s8s8s32_bt if w["bcm"] else t.gemm_s8s8s32
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    args = [(M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0), c.data_ptr(), c.stride(0), sh)
+            for (a, b, c) in sets]
+    for i in range(warmup):
+        st = fn(*args[i % nsets])
+        assert st == t.OK, t.tdi8_status_string(st)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        fn(*args[i % nsets])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / steps
+    kern_ms = ev0.elapsed_time(ev1) / steps
+    return wall_ms, kern_ms, t.select_tile_config(M, N, K), nsets, A, Bs, sets
+
+
+def cpu_baseline(w, A, Bs, budget_s=12.0):
+    """The oracle, as it is, on a bounded row sample of the same product."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    M, N, K = w["M"], w["N"], w["K"]
+    threads = oracle.num_threads()
+    rows = min(M, 2 * threads)
+    t0 = time.perf_counter()
+    oracle.gemm(np.ascontiguousarray(A[:rows]), Bs, w["bcm"], M=rows, N=N, K=K)
+    dt = max(time.perf_counter() - t0, 1e-4)
+    rows = int(max(1, min(M, rows * budget_s / dt)))
+    rows = max(threads, rows - rows % threads) if rows >= threads else rows
+    t0 = time.perf_counter()
+    C = oracle.gemm(np.ascontiguousarray(A[:rows]), Bs, w["bcm"], M=rows, N=N, K=K)
+    dt = time.perf_counter() - t0
+    assert C.shape == (rows, N)
+    return {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {rows} of {M} rows of C for the {M}x{N}x{K} product ({2 * rows * N * K:.3e} ops, "
+                      f"{dt:.1f} s, OpenMP over rows)"}
+
+
+def check_sample(w, A, Bs, C_dev, n=256):
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(1)
+    rows = rng.integers(0, w["M"], n)
+    cols = rng.integers(0, w["N"], n)
+    got = C_dev.cpu().numpy()[rows, cols]
+    want = oracle.gemm_elements(A, Bs, w["bcm"], w["K"], rows, cols)
+    return bool((got == want).all())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="square4096", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-skinny", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(sharding across GPUs is described in the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_dense_int8_amd as t
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log(f"[bench] device {props.name} {props.gcnArchName} CUs={props.multi_processor_count}")
+
+    w = WORKLOADS[args.workload]
+    M, N, K = w["M"], w["N"], w["K"]
+    ops = 2.0 * M * N * K
+    log(f"[bench] {args.workload}: warmup {args.warmup}, steps {args.steps}")
+    wall_ms, kern_ms, cfg, nsets, A, Bs, sets = time_workload(t, w, args.steps, args.warmup)
+    ok = check_sample(w, A, Bs, sets[0][2])
+    value = ops / (wall_ms * 1e-3) / 1e12
+    achieved = ops / (kern_ms * 1e-3) / 1e12
+    info = t.tile_config_info(cfg)
+    log(f"[bench] config {cfg} ({info.block_m}x{info.block_n}x{info.block_k}) wall {wall_ms * 1e3:.2f} us/step, "
+        f"kernel {kern_ms * 1e3:.2f} us, {achieved:.1f} TOPS, sample parity {ok}")
+    result = {
+        "metric": "INT8 GEMM TOPS (int32 acc) at 4096^3 and M=16 skinny; % of MFMA/HBM roofline",
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": w["desc"], "M": M, "N": N, "K": K,
+                   "b_layout": "column-major" if w["bcm"] else "row-major",
+                   "tile_config": cfg, "block_tile": [info.block_m, info.block_n, info.block_k],
+                   "rotating_input_sets": nsets, "sample_parity": ok},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_PEAK_TOPS, "unit": "TOP/s",
+                     "frac": round(achieved / MFMA_PEAK_TOPS, 4), "traffic": traffic_for(args.workload)},
+    }
+    if args.workload in ("skinny16", "ragged", "single256"):
+        byts = M * K + K * N + 4 * M * N
+        gbs = byts / (kern_ms * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(args.workload)}
+    del sets
+    torch.cuda.empty_cache()
+
+    if not args.no_skinny and args.workload == "square4096":
+        ws = WORKLOADS["skinny16"]
+        s_wall, s_kern, s_cfg, s_sets, sA, sB, ssets = time_workload(t, ws, max(args.steps, 200), args.warmup)
+        s_ok = check_sample(ws, sA, sB, ssets[0][2])
+        byts = ws["M"] * ws["K"] + ws["K"] * ws["N"] + 4 * ws["M"] * ws["N"]
+        gbs = byts / (s_kern * 1e-3) / 1e9
+        sops = 2.0 * ws["M"] * ws["N"] * ws["K"]
+        log(f"[bench] skinny16 config {s_cfg}: wall {s_wall * 1e3:.2f} us, kernel {s_kern * 1e3:.2f} us, "
+            f"{gbs:.0f} GB/s, parity {s_ok}")
+        result["skinny"] = {"workload": ws["desc"], "tile_config": s_cfg, "rotating_input_sets": s_sets,
+                            "value": round(sops / (s_wall * 1e-3) / 1e12, 3), "unit": "TOPS",
+                            "ms_per_step": round(s_wall, 6), "sample_parity": s_ok,
+                            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                         "traffic": traffic_for("skinny16")}}
+        del ssets
+
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(w, A, Bs)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

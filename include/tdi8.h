@@ -1,0 +1,168 @@
+/*
+ * tdi8.h -- C ABI of the MI355X (gfx950) tiled int8 matrix-multiply library.
+ *
+ * Operation.  C = A x B with signed int8 A (M x K) and B (K x N) and int32 C
+ * (M x N): C[i][j] = sum_k A[i][k] * B[k][j], accumulated in int32.  This is
+ * the product the TPU notes describe being fed, in passes, through a 256 x 256
+ * INT8 multiply-accumulate array ("Motivation for and Evaluation of the First
+ * Tensor Processing Unit" notes, sections "TPU介绍" and "TPU使用的技术"), and
+ * the matrix multiply whose tiling the CUDA tutorial analyses ("CUDA编程实践",
+ * section 3).  The kernel that runs is chosen per problem size from a table
+ * of compiled tile configurations, as the system of patent application
+ * CN114238853A does (claim 7: one kernel compiled per configuration, the
+ * configuration parameters being the kernel's template parameters, the best
+ * one selected at run time from the input size).
+ *
+ * Results are exact: every partial sum is an int32 and integer addition is
+ * associative, so the bytes of C do not depend on the tiling, the K split or
+ * the order of accumulation.  C is defined modulo 2^32 (two's-complement
+ * wrap); no wrap occurs while K <= 131071.
+ *
+ * Memory.  A, B and C are device pointers (hipMalloc'd, or a torch tensor's
+ * data_ptr()) owned by the caller.  The library allocates nothing and keeps no
+ * pointer after a call returns.  A and B are read only.  Only the window
+ * C[0:M, 0:N] is written; bytes of C's rows beyond column N (row padding up to
+ * ldc) are never touched.
+ *
+ * Layouts (all leading dimensions in elements):
+ *   A  row-major:        A(i,k) at A[i*lda + k],  lda >= K
+ *   B  row-major:        B(k,j) at B[k*ldb + j],  ldb >= N   (gemm_s8s8s32)
+ *   B  column-major:     B(k,j) at B[j*ldb + k],  ldb >= K   (gemm_s8s8s32_bt)
+ *   C  row-major:        C(i,j) at C[i*ldc + j],  ldc >= N
+ * Any pointer alignment and any leading dimension are accepted; 16-byte
+ * aligned operands whose sizes are tile multiples take the unpredicated fast
+ * kernels, the rest take the predicated tail kernels.
+ *
+ * Streams and errors.  Calls are asynchronous: work is enqueued on `stream`
+ * (0 = the null stream) and the call returns without waiting.  All argument
+ * checks run on the host before anything is enqueued; a call that returns an
+ * error has enqueued nothing.  A failed kernel launch returns TDI8_ERR_HIP
+ * and tdi8_last_hip_error() gives the hipError_t.  Faults inside a kernel
+ * surface at the caller's next synchronisation.  Nothing is printed.
+ *
+ * Threads.  Initialisation (device query, per-kernel occupancy) happens once
+ * per device on first use and is thread safe; afterwards every entry point is
+ * re-entrant.  Calls on one stream execute in order.
+ */
+#ifndef TDI8_H
+#define TDI8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same opaque handle type as HIP's own declaration. */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum {
+    TDI8_OK = 0,
+    TDI8_ERR_INVALID_VALUE = -1,     /* M, N or K < 0, or a leading dimension too small */
+    TDI8_ERR_NULL_POINTER = -2,      /* a pointer the call must dereference is NULL */
+    TDI8_ERR_ALIASING = -3,          /* C's window overlaps the bytes of A or B that are read */
+    TDI8_ERR_UNSUPPORTED_DEVICE = -4,/* the current device is not gfx950 */
+    TDI8_ERR_BAD_CONFIG = -5,        /* unknown configuration id, or it cannot run this shape */
+    TDI8_ERR_HIP = -6                /* a HIP runtime call failed; see tdi8_last_hip_error() */
+} tdi8_status;
+
+/* Route by which a configuration is reached in the selection. */
+typedef enum {
+    TDI8_ROUTE_GENERAL = 0,   /* survived the fill-the-compute-units step */
+    TDI8_ROUTE_FALLBACK = 1,  /* reuse-1 fallback of the fill step */
+    TDI8_ROUTE_SKINNY = 2     /* fallback with M small enough for the skinny family */
+} tdi8_route;
+
+/* C = A x B, A row-major M x K, B row-major K x N, C row-major M x N.
+ * M == 0 or N == 0: nothing is enqueued.  K == 0: the C window is set to 0.
+ * Returns TDI8_OK or a negative tdi8_status. */
+int gemm_s8s8s32(int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
+                 int32_t *C, int ldc, hipStream_t stream);
+
+/* Same as gemm_s8s8s32 with B column-major: B(k,j) at B[j*ldb + k], ldb >= K
+ * (B stored N x K with K contiguous, as inference weights usually are). */
+int gemm_s8s8s32_bt(int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
+                    int32_t *C, int ldc, hipStream_t stream);
+
+/* Same product computed with a given configuration id instead of the
+ * selected one (b_col_major selects the B layout).  Any general
+ * configuration runs any shape; a skinny configuration needs M <= its block
+ * height times 65535 (TDI8_ERR_BAD_CONFIG otherwise).  For tests and the
+ * bench, which sweep every compiled configuration. */
+int gemm_s8s8s32_with_config(int config_id, int b_col_major, int M, int N, int K,
+                             const int8_t *A, int lda, const int8_t *B, int ldb,
+                             int32_t *C, int ldc, hipStream_t stream);
+
+/* Configuration id that gemm_s8s8s32 / gemm_s8s8s32_bt use for an M x K by
+ * K x N product on the current device (>= 0), or a negative tdi8_status.
+ * The five steps of patent application CN114238853A claim 1 (claims 2-6 give
+ * the details): enumerate the compiled configurations; keep those whose
+ * register-limited active threads per compute unit reach the threshold;
+ * keep those launching at least (compute units x resident blocks per compute
+ * unit) blocks, or, if none does, every configuration reduced to reuse 1
+ * (then, for M <= 32, the skinny family); keep the largest compute-to-memory
+ * ratio BM*BN/(BM+BN); keep the fewest rounds of resident blocks; first in
+ * table order.  Host only; pure after the first call's initialisation. */
+int select_tile_config(int M, int N, int K);
+
+/* Static description of one compiled configuration plus its resource use on
+ * the current device (filled in by the initialisation). */
+typedef struct {
+    int id;
+    int family;          /* 0 general tiled kernel, 1 skinny (split-K across waves) kernel */
+    int mfma_m, mfma_n, mfma_k;  /* matrix-core instruction shape */
+    int waves_m, waves_n, waves_k;
+    int m_tiles, n_tiles;        /* per-wave instruction repeats (the claims' data reuse) */
+    int block_m, block_n, block_k;
+    int threads;
+    int lds_bytes;       /* static LDS per block */
+    int vgprs, agprs;    /* per lane, from the compiled kernel (0 before a device is seen) */
+    int blocks_per_cu;   /* resident blocks per compute unit, from the occupancy query */
+    int reuse1_id;       /* configuration with the same thread split and m_tiles = n_tiles = 1 */
+} tdi8_tile_config;
+
+/* Number of compiled configurations; ids are 0 .. count-1. */
+int tile_config_count(void);
+
+/* Copies the description of configuration `id` into *out.  Resource fields
+ * are filled only once a gfx950 device has been initialised (they are 0
+ * otherwise); no device is needed for the static fields. */
+int tile_config_info(int id, tdi8_tile_config *out);
+
+/* Hardware description used by the selection. */
+typedef struct {
+    int num_cu;                /* compute units */
+    int max_threads_per_block;
+    int min_active_threads;    /* claim-3 threshold on register-limited active threads per CU */
+    int skinny_max_m;          /* largest M routed to the skinny family */
+} tdi8_hw_info;
+
+typedef struct {
+    int id;
+    int route;                 /* tdi8_route */
+    int survivors[5];          /* candidates left after steps 1..5 */
+} tdi8_selection;
+
+/* The selection of select_tile_config on explicit hardware: `blocks_per_cu`
+ * holds one entry per configuration id (tile_config_count() entries).  Host
+ * only, needs no device; used to test the selection on described hardware.
+ * Returns the id (>= 0) or a negative tdi8_status; fills *out when non-NULL. */
+int select_tile_config_for(int M, int N, int K, const tdi8_hw_info *hw,
+                           const int *blocks_per_cu, tdi8_selection *out);
+
+/* Host-side argument check shared by every gemm entry point (no device
+ * needed): returns TDI8_OK or the status the entry point would return. */
+int tdi8_validate(int b_col_major, int M, int N, int K, const int8_t *A, int lda,
+                  const int8_t *B, int ldb, const int32_t *C, int ldc);
+
+/* Static string for a status code. */
+const char *tdi8_status_string(int status);
+
+/* hipError_t of the last failed HIP call made by this thread (0 if none). */
+int tdi8_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TDI8_H */

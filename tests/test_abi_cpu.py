@@ -1,0 +1,163 @@
+"""Host-side checks of the C-ABI library (no GPU): it loads, exports every
+function include/tdi8.h declares, validates arguments, and its selection
+agrees with the oracle's reading of the patent on described hardware."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_dense_int8_amd as t
+from oracle.selector import Cfg, Hw, select
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tdi8.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_functions_are_exported():
+    names = declared_functions()
+    assert "gemm_s8s8s32" in names and "select_tile_config" in names and len(names) >= 10
+    lib = ctypes.CDLL(t.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(t.EXPORTED) == names
+
+
+def test_nm_shows_c_linkage():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", t.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in declared_functions():
+        assert n in syms, n
+
+
+def test_status_strings():
+    for st in range(0, -7, -1):
+        assert t.tdi8_status_string(st) and t.tdi8_status_string(st) != "unknown status"
+    assert t.tdi8_status_string(-99) == "unknown status"
+
+
+A, B, C = 0x10000, 0x20000000, 0x40000000  # fake, well separated addresses; nothing is dereferenced
+
+
+@pytest.mark.parametrize("bcm", [0, 1])
+def test_validation(bcm):
+    v = t.tdi8_validate
+    ldb = 64 if bcm else 32
+    assert v(bcm, 16, 32, 64, A, 64, B, ldb, C, 32) == t.OK
+    assert v(bcm, -1, 32, 64, A, 64, B, ldb, C, 32) == t.ERR_INVALID_VALUE
+    assert v(bcm, 16, -1, 64, A, 64, B, ldb, C, 32) == t.ERR_INVALID_VALUE
+    assert v(bcm, 16, 32, -5, A, 64, B, ldb, C, 32) == t.ERR_INVALID_VALUE
+    assert v(bcm, 16, 32, 64, A, 63, B, ldb, C, 32) == t.ERR_INVALID_VALUE       # lda < K
+    assert v(bcm, 16, 32, 64, A, 64, B, ldb - 1, C, 32) == t.ERR_INVALID_VALUE   # ldb too small
+    assert v(bcm, 16, 32, 64, A, 64, B, ldb, C, 31) == t.ERR_INVALID_VALUE       # ldc < N
+    assert v(bcm, 16, 32, 64, 0, 64, B, ldb, C, 32) == t.ERR_NULL_POINTER
+    assert v(bcm, 16, 32, 64, A, 64, 0, ldb, C, 32) == t.ERR_NULL_POINTER
+    assert v(bcm, 16, 32, 64, A, 64, B, ldb, 0, 32) == t.ERR_NULL_POINTER
+    # empty problems need no pointers; K == 0 needs only C
+    assert v(bcm, 0, 32, 64, 0, 64, 0, ldb, 0, 32) == t.OK
+    assert v(bcm, 16, 0, 64, 0, 64, 0, max(ldb, 64), 0, 1) == t.OK
+    assert v(bcm, 16, 32, 0, 0, 1, 0, 32, C, 32) == t.OK
+    assert v(bcm, 16, 32, 0, 0, 1, 0, 32, 0, 32) == t.ERR_NULL_POINTER
+    # C overlapping A or B
+    assert v(bcm, 16, 32, 64, A, 64, B, ldb, A + 100, 32) == t.ERR_ALIASING
+    assert v(bcm, 16, 32, 64, A, 64, B, ldb, B + 8, 32) == t.ERR_ALIASING
+    assert v(bcm, 16, 32, 64, A, 64, B, ldb, A - 4 * (15 * 32 + 32) + 1, 32) == t.ERR_ALIASING
+    assert v(bcm, 16, 32, 64, A, 64, B, ldb, A - 4 * (15 * 32 + 32), 32) == t.OK  # ends exactly at A
+
+
+def test_entry_points_reject_before_any_device_work():
+    # invalid arguments are refused on the host, with no device present
+    assert t.gemm_s8s8s32(-1, 4, 4, A, 4, B, 4, C, 4, 0) == t.ERR_INVALID_VALUE
+    assert t.gemm_s8s8s32_bt(4, 4, 4, A, 4, B, 3, C, 4, 0) == t.ERR_INVALID_VALUE
+    assert t.gemm_s8s8s32_with_config(99, 1, 4, 4, 4, A, 4, B, 4, C, 4, 0) == t.ERR_BAD_CONFIG
+    assert t.gemm_s8s8s32_with_config(-1, 1, 4, 4, 4, A, 4, B, 4, C, 4, 0) == t.ERR_BAD_CONFIG
+    assert t.gemm_s8s8s32(0, 4, 4, 0, 4, 0, 4, 0, 4, 0) == t.OK
+    assert t.select_tile_config(-1, 1, 1) == t.ERR_INVALID_VALUE
+
+
+def library_table():
+    return [t.tile_config_info(i) for i in range(t.tile_config_count())]
+
+
+def test_config_table_shape():
+    tab = library_table()
+    assert [c.id for c in tab] == list(range(len(tab)))
+    for c in tab:
+        assert c.block_m == c.waves_m * c.mfma_m * c.m_tiles
+        assert c.block_n == c.waves_n * c.mfma_n * c.n_tiles
+        assert c.threads == 64 * c.waves_m * c.waves_n * c.waves_k
+        assert c.mfma_k == (32 if c.mfma_m == 32 else 64)
+        sib = tab[c.reuse1_id]
+        assert (sib.family, sib.mfma_m, sib.waves_m, sib.waves_n, sib.waves_k, sib.block_k, sib.m_tiles,
+                sib.n_tiles) == (c.family, c.mfma_m, c.waves_m, c.waves_n, c.waves_k, c.block_k, 1, 1)
+        if c.family == 0:
+            assert c.lds_bytes == 2 * (c.block_m + c.block_n) * c.block_k <= 160 * 1024
+    assert any(c.family == 1 and c.block_m == 16 for c in tab)
+    assert any(c.family == 1 and c.block_m == 32 for c in tab)
+
+
+def oracle_table(bpc):
+    fam = {0: "general", 1: "skinny"}
+    return [Cfg(c.id, fam[c.family], c.mfma_m, c.mfma_n, c.waves_m, c.waves_n, c.m_tiles, c.n_tiles,
+                c.block_k, c.threads, bpc[c.id]) for c in library_table()]
+
+
+def fake_bpc(lds_per_cu=160 * 1024, waves_per_cu=32):
+    """Resident blocks per CU from LDS and wave slots, a stand-in for the occupancy query."""
+    out = []
+    for c in library_table():
+        by_lds = lds_per_cu // c.lds_bytes
+        by_waves = waves_per_cu // (c.threads // 64)
+        out.append(max(0, min(by_lds, by_waves, 8)))
+    return out
+
+
+HARDWARE = [
+    (Hw(256, 1024, 256, 32), fake_bpc()),
+    (Hw(256, 1024, 256, 32), [1] * 15),
+    (Hw(304, 1024, 256, 32), fake_bpc(64 * 1024)),
+    (Hw(80, 256, 128, 16), fake_bpc(64 * 1024, 16)),
+    (Hw(256, 1024, 1024, 32), fake_bpc()),
+]
+SHAPES = [(m, n) for m in (1, 7, 16, 17, 32, 33, 64, 100, 256, 1000, 4096, 16384)
+          for n in (1, 16, 100, 256, 3000, 4096, 8192, 16384)]
+
+
+@pytest.mark.parametrize("hw_index", range(len(HARDWARE)))
+def test_selection_matches_oracle_reading(hw_index):
+    hw, bpc = HARDWARE[hw_index]
+    bpc = list(bpc)[:t.tile_config_count()]
+    hwc = t.HwInfo(hw.num_cu, hw.max_threads_per_block, hw.min_active_threads, hw.skinny_max_m)
+    table = oracle_table(bpc)
+    for m, n in SHAPES:
+        try:
+            want = select(m, n, 512, hw, table)
+        except ValueError:
+            with pytest.raises(t.TDI8Error):
+                t.select_tile_config_for(m, n, 512, hwc, bpc)
+            continue
+        got = t.select_tile_config_for(m, n, 512, hwc, bpc)
+        assert (got.id, got.route) == (want.id, want.route), (m, n, want.trace)
+        assert got.survivors[3] == len(want.trace["step4"]) and got.survivors[4] == len(want.trace["step5"])
+
+
+def test_mi355x_expectations():
+    """With the MI355X description and LDS/wave-slot occupancy, the selection
+    routes the five workloads as the method intends."""
+    hwc = t.HwInfo(256, 1024, 256, 32)
+    bpc = fake_bpc()
+    tab = library_table()
+    s = t.select_tile_config_for(4096, 4096, 4096, hwc, bpc)
+    assert s.route == t.ROUTE_GENERAL and (tab[s.id].block_m, tab[s.id].block_n) == (256, 256)
+    s = t.select_tile_config_for(16384, 16384, 8192, hwc, bpc)
+    assert s.route == t.ROUTE_GENERAL and (tab[s.id].block_m, tab[s.id].block_n) == (256, 256)
+    s = t.select_tile_config_for(16, 4096, 4096, hwc, bpc)
+    assert s.route == t.ROUTE_SKINNY and tab[s.id].block_m == 16
+    s = t.select_tile_config_for(256, 256, 256, hwc, bpc)
+    assert s.route == t.ROUTE_FALLBACK and tab[s.id].m_tiles == tab[s.id].n_tiles == 1

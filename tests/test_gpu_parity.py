@@ -1,0 +1,228 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI.
+
+Integer work, so the bar is bit-exact equality on every compared element.
+Small and ragged shapes are compared in full for every compiled
+configuration and both B layouts; the five workload shapes are compared in
+full where the oracle finishes in seconds, otherwise on sampled elements
+(whole first/last rows and columns plus random positions) together with a
+Freivalds product check over the whole of C."""
+import numpy as np
+import pytest
+
+import synthetic
+from helpers import DeviceCase, check_case, note
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiled_dense_int8_amd as t
+    return t
+
+
+def table(t):
+    return [t.tile_config_info(i) for i in range(t.tile_config_count())]
+
+
+def shapes_for(c):
+    BM, BN, BK = c.block_m, c.block_n, c.block_k
+    out = [(BM, BN, BK), (2 * BM, 2 * BN, 2 * BK), (BM + 1, BN - 1, BK + 27), (1, 1, 1), (17, 33, 63),
+           (3, 200, 4), (255, 257, 777), (64, 64, 65)]
+    if c.family == 1:
+        out += [(BM, 64, 64), (BM, 128, 256)]
+    return out
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_every_config_small_and_ragged(lib, bcm):
+    t = lib
+    for c in table(t):
+        for (M, N, K) in shapes_for(c):
+            A, B = synthetic.gemm_inputs(M, N, K, seed=M + 7 * N + 13 * K)
+            check_case(DeviceCase(A, B, bcm), f"with_config[{c.id}]", config=c.id)
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_identity_and_permutation_layout_probe(lib, bcm):
+    """A = I gives C = B and A = P gives permuted rows of B: pins the
+    accumulator-to-(row, column) map of every configuration."""
+    t = lib
+    rng = np.random.default_rng(0)
+    for c in table(t):
+        K = 64 if c.family == 1 else c.block_k
+        M = K
+        N = max(c.block_n, 64)
+        B = rng.integers(-128, 128, size=(K, N)).astype(np.int8)
+        eye = np.eye(K, dtype=np.int8)
+        check_case(DeviceCase(eye, B, bcm), f"identity cfg{c.id}", config=c.id, expect=B.astype(np.int32))
+        perm = rng.permutation(K)
+        check_case(DeviceCase(eye[perm], B, bcm), f"perm cfg{c.id}", config=c.id,
+                   expect=B[perm].astype(np.int32))
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_padded_and_misaligned_operands(lib, bcm):
+    t = lib
+    M, N, K = 70, 90, 150
+    A, B = synthetic.gemm_inputs(M, N, K, seed=4)
+    bk = N if not bcm else K
+    for c in table(t):
+        for (lda, ldb, ldc, offs) in [(K + 1, bk + 3, N + 1, (0, 0, 0)), (K + 16, bk + 16, N + 4, (1, 2, 1)),
+                                      (K, bk, N, (3, 5, 2)), (K + 32, bk + 64, N + 8, (16, 16, 4))]:
+            case = DeviceCase(A, B, bcm, lda=lda, ldb=ldb, ldc=ldc, offsets=offs)
+            check_case(case, f"padded cfg{c.id} offs={offs}", config=c.id)
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_selected_entry_edge_shapes(lib, bcm):
+    for (M, N, K) in [(1, 1, 1), (1, 4096, 4096), (32, 4096, 256), (33, 100, 1000), (16, 8192, 512),
+                      (4096, 16, 300), (257, 255, 64), (512, 512, 27), (300, 300, 4)]:
+        A, B = synthetic.gemm_inputs(M, N, K, seed=9)
+        check_case(DeviceCase(A, B, bcm), "selected")
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_zero_sizes(lib, bcm):
+    t = lib
+    # K = 0: the C window becomes 0, padding untouched
+    A = np.zeros((5, 0), np.int8)
+    B = np.zeros((0, 7), np.int8)
+    case = DeviceCase(A, B, bcm, lda=1, ldb=1 if bcm else 7, ldc=9)
+    check_case(case, "K=0", expect=np.zeros((5, 7), np.int32))
+    for cid in range(t.tile_config_count()):
+        case = DeviceCase(A, B, bcm, lda=1, ldb=1 if bcm else 7, ldc=9)
+        check_case(case, f"K=0 cfg{cid}", config=cid, expect=np.zeros((5, 7), np.int32))
+    # M = 0 / N = 0: nothing is written
+    for (M, N) in [(0, 5), (5, 0)]:
+        A, B = synthetic.gemm_inputs(M, N, 8, seed=1)
+        case = DeviceCase(A, B, bcm, ldc=max(N, 1))
+        assert case.run(None) == t.OK
+        _, rest = case.result()
+        assert (rest == -123456789).all()
+
+
+def test_extreme_values_closed_forms(lib):
+    for bcm in (True, False):
+        for (M, N, K) in [(256, 256, 256), (16, 4096, 4096), (100, 50, 777)]:
+            lo = np.full((M, K), -128, np.int8)
+            lob = np.full((K, N), -128, np.int8)
+            check_case(DeviceCase(lo, lob, bcm), "all -128", expect=np.full((M, N), 16384 * K, np.int32))
+            hi = np.full((M, K), 127, np.int8)
+            check_case(DeviceCase(hi, lob, bcm), "127 x -128", expect=np.full((M, N), -16256 * K, np.int32))
+
+
+def test_deterministic_bytes(lib):
+    A, B = synthetic.gemm_inputs(1000, 3000, 777, seed=0)
+    case = DeviceCase(A, B, True)
+    first = None
+    for _ in range(5):
+        case.c_buf.fill_(-123456789)
+        assert case.run(None) == lib.OK
+        C, _ = case.result()
+        first = C if first is None else first
+        assert np.array_equal(C, first)
+
+
+def test_non_default_stream(lib):
+    A, B = synthetic.gemm_inputs(256, 256, 256, seed=3)
+    case = DeviceCase(A, B, False)
+    s = torch.cuda.Stream()
+    note("[case] stream launch 256^3")
+    with torch.cuda.stream(s):
+        assert case.run(None, stream=s.cuda_stream) == lib.OK
+    s.synchronize()
+    C, rest = case.result()
+    assert np.array_equal(C, case.oracle()) and (rest == -123456789).all()
+
+
+def test_selection_on_device_matches_oracle(lib):
+    from oracle.selector import Cfg, Hw, select
+    t = lib
+    props = torch.cuda.get_device_properties(0)
+    assert props.gcnArchName.startswith("gfx950")
+    tab = table(t)
+    assert all(c.blocks_per_cu >= 1 for c in tab)
+    fam = {0: "general", 1: "skinny"}
+    otab = [Cfg(c.id, fam[c.family], c.mfma_m, c.mfma_n, c.waves_m, c.waves_n, c.m_tiles, c.n_tiles,
+                c.block_k, c.threads, c.blocks_per_cu) for c in tab]
+    hw = Hw(num_cu=props.multi_processor_count, max_threads_per_block=1024, min_active_threads=256,
+            skinny_max_m=32)
+    for (M, N, K) in [(256, 256, 256), (4096, 4096, 4096), (16, 4096, 4096), (1000, 3000, 777),
+                      (16384, 16384, 8192), (1, 1, 1), (33, 4096, 4096)]:
+        want = select(M, N, K, hw, otab)
+        assert t.select_tile_config(M, N, K) == want.id, (M, N, K, want.trace)
+    note(f"[info] device CUs={props.multi_processor_count} "
+         f"bpc={[c.blocks_per_cu for c in tab]} regs={[c.vgprs for c in tab]}")
+
+
+# ---- the five workloads -------------------------------------------------------------
+
+def sampled_check(C_dev, A_store, B_store, bcm, M, N, K, seed, n_random=4096, freivalds=2):
+    import oracle
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([np.zeros(N, np.int64), np.full(N, M - 1), np.arange(M), np.arange(M),
+                           rng.integers(0, M, n_random)])
+    cols = np.concatenate([np.arange(N), np.arange(N), np.zeros(M, np.int64), np.full(M, N - 1),
+                           rng.integers(0, N, n_random)])
+    C = C_dev.cpu().numpy()
+    want = oracle.gemm_elements(A_store, B_store, bcm, K, rows, cols)
+    got = C[rows, cols]
+    assert np.array_equal(got, want), f"{int((got != want).sum())} sampled mismatches"
+    if freivalds:
+        # exact in float64: every partial sum is an integer below 2**53
+        X = synthetic.freivalds_vectors(N, freivalds, seed).astype(np.float64)
+        B_log = B_store[:N, :K].T if bcm else B_store[:K, :N]
+        BX = np.zeros((K, freivalds))
+        for k0 in range(0, K, 2048):
+            BX[k0:k0 + 2048] = B_log[k0:k0 + 2048].astype(np.float64) @ X.T
+        for m0 in range(0, M, 2048):
+            left = C[m0:m0 + 2048].astype(np.float64) @ X.T
+            right = A_store[m0:m0 + 2048, :K].astype(np.float64) @ BX
+            assert np.array_equal(left, right), f"Freivalds mismatch in rows {m0}.."
+
+
+WORKLOADS = {
+    "cfg1_256": (256, 256, 256),
+    "cfg2_4096": (4096, 4096, 4096),
+    "cfg3_skinny": (16, 4096, 4096),
+    "cfg4_ragged": (1000, 3000, 777),
+}
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("bcm", [True, False])
+def test_workloads_seeds(lib, name, bcm):
+    M, N, K = WORKLOADS[name]
+    for seed in (0, 1, 2):
+        A, B = synthetic.gemm_inputs(M, N, K, seed)
+        case = DeviceCase(A, B, bcm)
+        cfg = lib.select_tile_config(M, N, K)
+        note(f"[case] {name} seed={seed} bcm={bcm} selected={cfg}")
+        if M * N * K <= 4 * 10 ** 9:
+            check_case(case, f"{name} seed {seed}")
+        else:
+            assert case.run(None) == lib.OK
+            torch.cuda.synchronize()
+            win = case.c_buf[:M * N].view(M, N)
+            sampled_check(win, case.A_store, case.B_store, bcm, M, N, K, seed)
+            assert (case.c_buf[M * N:].cpu().numpy() == -123456789).all()
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_workload_large_16384(lib, bcm):
+    M, N, K = 16384, 16384, 8192
+    note(f"[case] cfg5 16384x16384x8192 bcm={bcm} generating")
+    A, B = synthetic.gemm_inputs(M, N, K, 0)
+    A_dev = torch.from_numpy(A).cuda()
+    Bs = synthetic.store_b(B, bcm)
+    B_dev = torch.from_numpy(Bs).cuda()
+    C_dev = torch.full((M, N), -123456789, dtype=torch.int32, device="cuda")
+    note(f"[case] cfg5 launch selected={lib.select_tile_config(M, N, K)}")
+    lib.gemm(A_dev, B_dev, bcm, out=C_dev)
+    torch.cuda.synchronize()
+    sampled_check(C_dev, A, Bs, bcm, M, N, K, seed=0, n_random=8192, freivalds=2)

@@ -1,0 +1,180 @@
+"""Python binding of libtdi8.so, the gfx950 tiled int8 GEMM library.
+
+Argument marshalling only: every step of the product runs in the library's
+HIP kernels (C ABI in include/tdi8.h).  The names mirror the C entry points;
+``gemm`` is a convenience wrapper that takes torch tensors, whose only role
+is device memory and the current stream.
+
+There is no fallback: if libtdi8.so is missing or fails to load, importing
+this package raises.  Build it with ``python tiled_dense_int8_amd/build.py``
+(or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads torch's HIP runtime first, so the library binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtdi8.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with tiled_dense_int8_amd/build.py")
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK = 0
+ERR_INVALID_VALUE = -1
+ERR_NULL_POINTER = -2
+ERR_ALIASING = -3
+ERR_UNSUPPORTED_DEVICE = -4
+ERR_BAD_CONFIG = -5
+ERR_HIP = -6
+
+ROUTE_GENERAL, ROUTE_FALLBACK, ROUTE_SKINNY = 0, 1, 2
+
+
+class TileConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "id", "family", "mfma_m", "mfma_n", "mfma_k", "waves_m", "waves_n", "waves_k",
+        "m_tiles", "n_tiles", "block_m", "block_n", "block_k", "threads", "lds_bytes",
+        "vgprs", "agprs", "blocks_per_cu", "reuse1_id")]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class HwInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "num_cu", "max_threads_per_block", "min_active_threads", "skinny_max_m")]
+
+
+class Selection(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int), ("route", ctypes.c_int), ("survivors", ctypes.c_int * 5)]
+
+
+_i, _p = ctypes.c_int, ctypes.c_void_p
+_GEMM_ARGS = [_i, _i, _i, _p, _i, _p, _i, _p, _i, _p]
+_SIGNATURES = {
+    "gemm_s8s8s32": (_i, _GEMM_ARGS),
+    "gemm_s8s8s32_bt": (_i, _GEMM_ARGS),
+    "gemm_s8s8s32_with_config": (_i, [_i, _i] + _GEMM_ARGS),
+    "select_tile_config": (_i, [_i, _i, _i]),
+    "tile_config_count": (_i, []),
+    "tile_config_info": (_i, [_i, ctypes.POINTER(TileConfig)]),
+    "select_tile_config_for": (_i, [_i, _i, _i, ctypes.POINTER(HwInfo), ctypes.POINTER(_i),
+                                    ctypes.POINTER(Selection)]),
+    "tdi8_validate": (_i, [_i, _i, _i, _i, _p, _i, _p, _i, _p, _i]),
+    "tdi8_status_string": (ctypes.c_char_p, [_i]),
+    "tdi8_last_hip_error": (_i, []),
+}
+for _name, (_res, _args) in _SIGNATURES.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGNATURES)
+
+
+class TDI8Error(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        msg = tdi8_status_string(status)
+        if status == ERR_HIP:
+            msg += f" (hipError_t {tdi8_last_hip_error()})"
+        super().__init__(f"tdi8 status {status}: {msg}")
+
+
+# ----- the C entry points, same names and arguments -------------------------------
+
+def gemm_s8s8s32(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    return _lib.gemm_s8s8s32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_s8s8s32_bt(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    return _lib.gemm_s8s8s32_bt(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_s8s8s32_with_config(config_id, b_col_major, M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    return _lib.gemm_s8s8s32_with_config(config_id, 1 if b_col_major else 0, M, N, K, A, lda, B, ldb,
+                                         C, ldc, stream)
+
+
+def select_tile_config(M, N, K) -> int:
+    return _lib.select_tile_config(M, N, K)
+
+
+def tile_config_count() -> int:
+    return _lib.tile_config_count()
+
+
+def tile_config_info(config_id: int) -> TileConfig:
+    out = TileConfig()
+    st = _lib.tile_config_info(config_id, ctypes.byref(out))
+    if st != OK:
+        raise TDI8Error(st)
+    return out
+
+
+def select_tile_config_for(M, N, K, hw: HwInfo, blocks_per_cu) -> Selection:
+    arr = (ctypes.c_int * tile_config_count())(*blocks_per_cu)
+    out = Selection()
+    st = _lib.select_tile_config_for(M, N, K, ctypes.byref(hw), arr, ctypes.byref(out))
+    if st < 0:
+        raise TDI8Error(st)
+    return out
+
+
+def tdi8_validate(b_col_major, M, N, K, A, lda, B, ldb, C, ldc) -> int:
+    return _lib.tdi8_validate(1 if b_col_major else 0, M, N, K, A, lda, B, ldb, C, ldc)
+
+
+def tdi8_status_string(status: int) -> str:
+    return _lib.tdi8_status_string(status).decode()
+
+
+def tdi8_last_hip_error() -> int:
+    return _lib.tdi8_last_hip_error()
+
+
+# ----- torch convenience -----------------------------------------------------------
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def gemm(A: "torch.Tensor", B: "torch.Tensor", b_col_major: bool, out: "torch.Tensor | None" = None,
+         config: int | None = None, stream=None) -> "torch.Tensor":
+    """C = A x B on the GPU.
+
+    A: int8 (M, K) with unit column stride (row stride = lda).
+    B: int8 storage of the logical K x N matrix: (K, N) row-major if
+       b_col_major is False, (N, K) with K contiguous if True.
+    out: optional int32 (M, N) with unit column stride (row stride = ldc).
+    config: run this configuration id instead of the selected one.
+    """
+    if A.dtype != torch.int8 or B.dtype != torch.int8:
+        raise TypeError("A and B must be int8")
+    if A.dim() != 2 or B.dim() != 2 or A.stride(1) != 1 or B.stride(1) != 1:
+        raise ValueError("A and B must be 2-D with unit column stride")
+    M, K = A.shape
+    N = B.shape[0] if b_col_major else B.shape[1]
+    if (B.shape[1] if b_col_major else B.shape[0]) != K:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32, device=A.device)
+    if out.dtype != torch.int32 or out.dim() != 2 or tuple(out.shape) != (M, N) or out.stride(1) != 1:
+        raise ValueError("out must be int32 (M, N) with unit column stride")
+    lda, ldb, ldc = max(A.stride(0), 1), max(B.stride(0), 1), max(out.stride(0), 1)
+    s = _stream_handle(stream)
+    if config is None:
+        fn = gemm_s8s8s32_bt if b_col_major else gemm_s8s8s32
+        st = fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, s)
+    else:
+        st = gemm_s8s8s32_with_config(config, b_col_major, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                                      out.data_ptr(), ldc, s)
+    if st != OK:
+        raise TDI8Error(st)
+    return out

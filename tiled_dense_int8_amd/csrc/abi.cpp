@@ -1,0 +1,293 @@
+// C ABI entry points: argument checks, per-device initialisation, selection
+// and kernel launch.  The pages' launchers print the HIP error after each
+// launch (contest write-up, the NCHW_2_NHWC and Im2col launch wrappers); a
+// library returns it instead.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/tdi8.h"
+#include "kernel_table.h"
+#include "selector.h"
+#include "device_common.h"
+
+namespace tdi8 {
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = static_cast<int>(e);
+    return TDI8_ERR_HIP;
+}
+
+const KernelSet *kernels() {
+    static const KernelSet *table = [] {
+        static KernelSet ks[TDI8_NUM_CONFIGS];
+#define TDI8_CALL_REGISTER(ID, ...) register_cfg_##ID(&ks[ID]);
+        TDI8_CONFIG_LIST(TDI8_CALL_REGISTER)
+#undef TDI8_CALL_REGISTER
+        return ks;
+    }();
+    return table;
+}
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+    std::once_flag once;
+    int status = TDI8_OK;
+    int hip_error = 0;
+    tdi8_hw_info hw{};
+    int bpc[TDI8_NUM_CONFIGS] = {};
+    int regs[TDI8_NUM_CONFIGS] = {};
+    int lds[TDI8_NUM_CONFIGS] = {};
+};
+
+DeviceState g_devices[kMaxDevices];
+
+void init_device(DeviceState &ds, int dev) {
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) {
+        ds.status = TDI8_ERR_HIP;
+        ds.hip_error = static_cast<int>(e);
+        return;
+    }
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+        ds.status = TDI8_ERR_UNSUPPORTED_DEVICE;
+        return;
+    }
+    ds.hw.num_cu = prop.multiProcessorCount;
+    ds.hw.max_threads_per_block = prop.maxThreadsPerBlock;
+    ds.hw.min_active_threads = 4 * prop.warpSize;  // one wave on each of the 4 SIMDs of a CU
+    ds.hw.skinny_max_m = 32;
+    for (int id = 0; id < TDI8_NUM_CONFIGS; ++id) {
+        const StaticCfg c = static_cfg(id);
+        const void *k = kernels()[id].kernel[1][1];
+        hipFuncAttributes fa;
+        e = hipFuncGetAttributes(&fa, k);
+        if (e != hipSuccess) {
+            ds.status = TDI8_ERR_HIP;
+            ds.hip_error = static_cast<int>(e);
+            return;
+        }
+        int nb = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, c.threads, 0);
+        if (e != hipSuccess) {
+            ds.status = TDI8_ERR_HIP;
+            ds.hip_error = static_cast<int>(e);
+            return;
+        }
+        ds.bpc[id] = nb;
+        ds.regs[id] = fa.numRegs;
+        ds.lds[id] = static_cast<int>(fa.sharedSizeBytes);
+    }
+}
+
+// Initialised state of the current device, or nullptr with *status set.
+DeviceState *current_device(int *status) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *status = hip_fail(e);
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        *status = TDI8_ERR_UNSUPPORTED_DEVICE;
+        return nullptr;
+    }
+    DeviceState &ds = g_devices[dev];
+    std::call_once(ds.once, [&] { init_device(ds, dev); });
+    if (ds.status != TDI8_OK) {
+        if (ds.status == TDI8_ERR_HIP) g_last_hip_error = ds.hip_error;
+        *status = ds.status;
+        return nullptr;
+    }
+    return &ds;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
+           int32_t *C, int ldc, hipStream_t stream) {
+    const StaticCfg c = static_cfg(id);
+    GemmArgs g;
+    g.A = A;
+    g.B = B;
+    g.C = C;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.ldc = ldc;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    const bool c_ok = aligned(C, 16) && ldc % 4 == 0;
+    const bool a_ok = aligned(A, 16) && lda % 16 == 0;
+    dim3 grid, block(c.threads);
+    bool fast;
+    if (c.family == 0) {
+        const int64_t tm = (M + static_cast<int64_t>(c.bm) - 1) / c.bm;
+        const int64_t tn = (N + static_cast<int64_t>(c.bn) - 1) / c.bn;
+        if (tm * tn > INT_MAX / c.threads) return TDI8_ERR_INVALID_VALUE;
+        g.tiles_m = static_cast<int>(tm);
+        g.tiles_n = static_cast<int>(tn);
+        grid = dim3(static_cast<unsigned>(tm * tn));
+        const bool b_ok = bcol ? (aligned(B, 16) && ldb % 16 == 0) : (aligned(B, 4) && ldb % 4 == 0);
+        fast = M % c.bm == 0 && N % c.bn == 0 && K % c.bk == 0 && a_ok && b_ok && c_ok;
+    } else {
+        const int bn = bcol ? c.bn : 64;
+        const int64_t tm = (M + static_cast<int64_t>(c.bm) - 1) / c.bm;
+        const int64_t tn = (N + static_cast<int64_t>(bn) - 1) / bn;
+        if (tm > 65535) return TDI8_ERR_BAD_CONFIG;
+        if (tn > INT_MAX / c.threads) return TDI8_ERR_INVALID_VALUE;
+        g.tiles_m = static_cast<int>(tm);
+        g.tiles_n = static_cast<int>(tn);
+        grid = dim3(static_cast<unsigned>(tn), static_cast<unsigned>(tm));
+        if (bcol)
+            fast = M % c.bm == 0 && N % bn == 0 && K % c.bk == 0 && a_ok && aligned(B, 16) && ldb % 16 == 0 && c_ok;
+        else
+            fast = M % c.bm == 0 && N % bn == 0 && K % 64 == 0 && a_ok && aligned(B, 4) && ldb % 4 == 0 && c_ok;
+    }
+    const void *k = kernels()[id].kernel[bcol ? 1 : 0][fast ? 1 : 0];
+    void *args[] = {&g};
+    hipError_t e = hipLaunchKernel(k, grid, block, args, 0, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return TDI8_OK;
+}
+
+bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+int gemm_entry(int cfg, int bcol, int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
+               int32_t *C, int ldc, hipStream_t stream) {
+    int st = tdi8_validate(bcol, M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != TDI8_OK) return st;
+    if (cfg >= TDI8_NUM_CONFIGS || cfg < -1) return TDI8_ERR_BAD_CONFIG;
+    if (M == 0 || N == 0) return TDI8_OK;
+    DeviceState *ds = current_device(&st);
+    if (!ds) return st;
+    int id = cfg;
+    if (id < 0) {
+        id = select_config(M, N, K, ds->hw, ds->bpc, nullptr);
+        if (id < 0) return id;
+    }
+    return launch(id, bcol, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+}  // namespace
+}  // namespace tdi8
+
+using namespace tdi8;
+
+extern "C" {
+
+int tdi8_validate(int b_col_major, int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
+                  const int32_t *C, int ldc) {
+    if (M < 0 || N < 0 || K < 0) return TDI8_ERR_INVALID_VALUE;
+    const int kmin = K > 1 ? K : 1;
+    const int nmin = N > 1 ? N : 1;
+    if (lda < kmin || ldc < nmin || ldb < (b_col_major ? kmin : nmin)) return TDI8_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) return TDI8_OK;
+    if (!C) return TDI8_ERR_NULL_POINTER;
+    if (K == 0) return TDI8_OK;
+    if (!A || !B) return TDI8_ERR_NULL_POINTER;
+    const uintptr_t c0 = reinterpret_cast<uintptr_t>(C);
+    const uintptr_t c1 = c0 + 4 * (static_cast<uint64_t>(M - 1) * static_cast<uint64_t>(ldc) + N);
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(A);
+    const uintptr_t a1 = a0 + static_cast<uint64_t>(M - 1) * static_cast<uint64_t>(lda) + K;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(B);
+    const uintptr_t b1 = b0 + (b_col_major ? static_cast<uint64_t>(N - 1) * static_cast<uint64_t>(ldb) + K
+                                           : static_cast<uint64_t>(K - 1) * static_cast<uint64_t>(ldb) + N);
+    if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return TDI8_ERR_ALIASING;
+    return TDI8_OK;
+}
+
+int gemm_s8s8s32(int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb, int32_t *C, int ldc,
+                 hipStream_t stream) {
+    return gemm_entry(-1, 0, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_s8s8s32_bt(int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb, int32_t *C, int ldc,
+                    hipStream_t stream) {
+    return gemm_entry(-1, 1, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_s8s8s32_with_config(int config_id, int b_col_major, int M, int N, int K, const int8_t *A, int lda,
+                             const int8_t *B, int ldb, int32_t *C, int ldc, hipStream_t stream) {
+    if (config_id < 0 || config_id >= TDI8_NUM_CONFIGS) return TDI8_ERR_BAD_CONFIG;
+    return gemm_entry(config_id, b_col_major ? 1 : 0, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int select_tile_config(int M, int N, int K) {
+    if (M < 0 || N < 0 || K < 0) return TDI8_ERR_INVALID_VALUE;
+    int st = TDI8_OK;
+    DeviceState *ds = current_device(&st);
+    if (!ds) return st;
+    return select_config(M, N, K, ds->hw, ds->bpc, nullptr);
+}
+
+int select_tile_config_for(int M, int N, int K, const tdi8_hw_info *hw, const int *blocks_per_cu,
+                           tdi8_selection *out) {
+    if (M < 0 || N < 0 || K < 0) return TDI8_ERR_INVALID_VALUE;
+    if (!hw || !blocks_per_cu) return TDI8_ERR_NULL_POINTER;
+    if (hw->num_cu <= 0 || hw->max_threads_per_block <= 0) return TDI8_ERR_INVALID_VALUE;
+    return select_config(M, N, K, *hw, blocks_per_cu, out);
+}
+
+int tile_config_count(void) { return TDI8_NUM_CONFIGS; }
+
+int tile_config_info(int id, tdi8_tile_config *out) {
+    if (id < 0 || id >= TDI8_NUM_CONFIGS) return TDI8_ERR_BAD_CONFIG;
+    if (!out) return TDI8_ERR_NULL_POINTER;
+    const StaticCfg c = static_cfg(id);
+    tdi8_tile_config t{};
+    t.id = id;
+    t.family = c.family;
+    t.mfma_m = c.mf;
+    t.mfma_n = c.mf;
+    t.mfma_k = c.mfma_k;
+    t.waves_m = c.wm;
+    t.waves_n = c.wn;
+    t.waves_k = c.wk;
+    t.m_tiles = c.mt;
+    t.n_tiles = c.nt;
+    t.block_m = c.bm;
+    t.block_n = c.bn;
+    t.block_k = c.bk;
+    t.threads = c.threads;
+    t.lds_bytes = c.lds_bytes;
+    t.reuse1_id = c.reuse1_id;
+    int dev = -1;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+        int st = TDI8_OK;
+        DeviceState *ds = current_device(&st);
+        if (ds) {
+            t.vgprs = ds->regs[id];
+            t.agprs = 0;
+            t.blocks_per_cu = ds->bpc[id];
+            if (ds->lds[id] > 0) t.lds_bytes = ds->lds[id];
+        }
+    }
+    *out = t;
+    return TDI8_OK;
+}
+
+const char *tdi8_status_string(int status) {
+    switch (status) {
+        case TDI8_OK: return "ok";
+        case TDI8_ERR_INVALID_VALUE: return "invalid value (negative size or leading dimension too small)";
+        case TDI8_ERR_NULL_POINTER: return "null pointer";
+        case TDI8_ERR_ALIASING: return "C overlaps A or B";
+        case TDI8_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
+        case TDI8_ERR_BAD_CONFIG: return "bad configuration id for this shape";
+        case TDI8_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int tdi8_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

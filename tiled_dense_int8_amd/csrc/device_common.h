@@ -1,0 +1,95 @@
+// Device-side helpers shared by the gfx950 GEMM kernels: vector types,
+// masked loads for the tail kernels, C stores.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tdi8 {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+
+// Kernel arguments, passed by value.  Leading dimensions in elements.
+struct GemmArgs {
+    const int8_t *A;
+    const int8_t *B;
+    int32_t *C;
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+    int tiles_m, tiles_n;  // block tiles along M and N
+};
+
+__device__ __forceinline__ int clamp16(int v) { return v < 0 ? 0 : (v > 16 ? 16 : v); }
+__device__ __forceinline__ int clamp4(int v) { return v < 0 ? 0 : (v > 4 ? 4 : v); }
+
+// 16 bytes at p; p is 16-byte aligned (unpredicated kernels).
+__device__ __forceinline__ i32x4 load16(const int8_t *p) {
+    return *reinterpret_cast<const i32x4 *>(p);
+}
+
+// Keep the low `nvalid` bytes (0..4) of a dword.
+__device__ __forceinline__ uint32_t keep_bytes(uint32_t w, int nvalid) {
+    return nvalid >= 4 ? w : (nvalid <= 0 ? 0u : (w & ((1u << (8 * nvalid)) - 1u)));
+}
+
+// The first `nvalid` (0..16) bytes at p, any alignment, zero beyond.
+// Only dwords holding at least one wanted byte are read; an aligned dword
+// never straddles a page, so nothing outside the operand's pages is touched.
+__device__ __forceinline__ i32x4 load16_masked(const int8_t *p, int nvalid) {
+    i32x4 r = {0, 0, 0, 0};
+    if (nvalid <= 0) return r;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    if (nvalid >= 16 && (a & 15) == 0) return load16(p);
+    const uint32_t s = static_cast<uint32_t>(a & 3);
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(a - s);
+    uint32_t d[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) d[i] = (4 * i < static_cast<int>(s) + nvalid) ? w[i] : 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        r[j] = static_cast<int32_t>(keep_bytes(__builtin_amdgcn_alignbyte(d[j + 1], d[j], s), nvalid - 4 * j));
+    return r;
+}
+
+// The first `nvalid` (0..4) bytes at p, any alignment, zero beyond.
+__device__ __forceinline__ uint32_t load4_masked(const int8_t *p, int nvalid) {
+    if (nvalid <= 0) return 0u;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    if (nvalid >= 4 && (a & 3) == 0) return *reinterpret_cast<const uint32_t *>(p);
+    const uint32_t s = static_cast<uint32_t>(a & 3);
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(a - s);
+    const uint32_t d0 = w[0];
+    const uint32_t d1 = (4 < static_cast<int>(s) + nvalid) ? w[1] : 0u;
+    return keep_bytes(__builtin_amdgcn_alignbyte(d1, d0, s), nvalid);
+}
+
+// 4x4 byte transpose: in[r] holds bytes (r,0..3); out[c] gets bytes (0..3,c).
+__device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int sh = 8 * c;
+        out[c] = ((in[0] >> sh) & 0xFFu) | (((in[1] >> sh) & 0xFFu) << 8) |
+                 (((in[2] >> sh) & 0xFFu) << 16) | (((in[3] >> sh) & 0xFFu) << 24);
+    }
+}
+
+// Four consecutive C elements of row m starting at column n.
+template <bool FAST>
+__device__ __forceinline__ void store4(const GemmArgs &g, int m, int n, i32x4 v) {
+    if (FAST) {
+        *reinterpret_cast<i32x4 *>(g.C + static_cast<int64_t>(m) * g.ldc + n) = v;
+        return;
+    }
+    if (m >= g.M) return;
+    int32_t *p = g.C + static_cast<int64_t>(m) * g.ldc + n;
+    if (n + 3 < g.N && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+        *reinterpret_cast<i32x4 *>(p) = v;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n + e < g.N) p[e] = v[e];
+    }
+}
+
+}  // namespace tdi8

@@ -1,0 +1,37 @@
+// Instantiates the kernels of configuration TDI8_CFG (set on the compiler
+// command line, one object per configuration) and registers their entry
+// points.  Patent application CN114238853A, claim 7: every configuration's
+// parameters become the kernel's template parameters and all are compiled.
+#include "kernel_table.h"
+#include "skinny_kernel.h"
+#include "tiled_kernel.h"
+
+#ifndef TDI8_CFG
+#error "TDI8_CFG must name a configuration id"
+#endif
+
+#define TDI8_CAT2(a, b) a##b
+#define TDI8_CAT(a, b) TDI8_CAT2(a, b)
+
+namespace tdi8 {
+
+template <class P, bool BCOL, bool FAST>
+static const void *entry() {
+    if constexpr (P::family == 0)
+        return reinterpret_cast<const void *>(
+            &gemm_tiled_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, BCOL, FAST>);
+    else if constexpr (BCOL)
+        return reinterpret_cast<const void *>(&gemm_skinny_kernel<P::mt, P::nt, P::wk, FAST>);
+    else
+        return reinterpret_cast<const void *>(&gemm_skinny_rr_kernel<P::mt, P::wk, FAST>);
+}
+
+void TDI8_CAT(register_cfg_, TDI8_CFG)(KernelSet *ks) {
+    using P = CfgParams<TDI8_CFG>;
+    ks->kernel[0][0] = entry<P, false, false>();
+    ks->kernel[0][1] = entry<P, false, true>();
+    ks->kernel[1][0] = entry<P, true, false>();
+    ks->kernel[1][1] = entry<P, true, true>();
+}
+
+}  // namespace tdi8

@@ -1,0 +1,32 @@
+// Host-side view of the compiled configurations: static parameters from the
+// configuration list and the kernel entry points of each one.
+#pragma once
+
+#include "configs.h"
+
+namespace tdi8 {
+
+template <int ID>
+struct CfgParams;
+
+#define TDI8_DEFINE_PARAMS(ID, FAM, MF_, WM_, WN_, WK_, MT_, NT_, BK_)                   \
+    template <>                                                                          \
+    struct CfgParams<ID> {                                                               \
+        static constexpr int family = FAM, mf = MF_, wm = WM_, wn = WN_, wk = WK_,       \
+                             mt = MT_, nt = NT_, bk = BK_;                               \
+    };
+TDI8_CONFIG_LIST(TDI8_DEFINE_PARAMS)
+#undef TDI8_DEFINE_PARAMS
+
+// kernel[b_col_major][fast]: host stubs of the four instantiations.
+struct KernelSet {
+    const void *kernel[2][2];
+};
+
+// One registration function per configuration, each defined in its own
+// translation unit so the instantiations compile in parallel.
+#define TDI8_DECLARE_REGISTER(ID, ...) void register_cfg_##ID(KernelSet *ks);
+TDI8_CONFIG_LIST(TDI8_DECLARE_REGISTER)
+#undef TDI8_DECLARE_REGISTER
+
+}  // namespace tdi8

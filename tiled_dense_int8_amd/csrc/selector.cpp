@@ -1,0 +1,188 @@
+// Tile-configuration selection: the five steps of patent application
+// CN114238853A claim 1, with claims 2-6 read for CDNA4.  Host-only, no HIP.
+//
+//  step 1  the candidates are the compiled configurations (claim 7);
+//  step 2  thread split along M and N: multiples of the matrix-core tile,
+//          each at least 16, at most max_threads_per_block threads (claim 2,
+//          matrix-unit case); drop configurations whose register-limited
+//          active threads per compute unit, blocks_per_cu * threads, stay
+//          below the threshold (claim 3, first alternative);
+//  step 3  Thread_Blocks = ceil(M / BM) * ceil(N / BN) must reach
+//          min_theory_block_num = num_cu * blocks_per_cu; if no configuration
+//          does, the size is too small to fill the compute units and every
+//          step-2 survivor is reduced to reuse 1 (m_tiles = n_tiles = 1: its
+//          reuse-1 sibling) and kept (claim 4).  For M <= skinny_max_m the
+//          candidates then become the skinny family with the smallest block
+//          height >= M, keeping those with at least one block per compute
+//          unit (all of them if none has);
+//  step 4  keep the largest compute-to-memory ratio of a K step,
+//          BM*BN*BK / (BM*BK + BK*BN) = BM*BN / (BM + BN), compared exactly
+//          by cross-multiplication (claim 5; the B tile width uses n_tiles);
+//  step 5  keep the fewest kernel rounds ceil(Thread_Blocks / (num_cu *
+//          blocks_per_cu)) (claim 6); remaining ties go to table order.
+#include "selector.h"
+
+#include <cstdint>
+
+namespace tdi8 {
+
+namespace {
+
+struct Desc {
+    int id, family, mf, wm, wn, wk, mt, nt, bk;
+};
+
+constexpr Desc kDesc[] = {
+#define TDI8_DESC(ID, FAM, MF, WM, WN, WK, MT, NT, BK) {ID, FAM, MF, WM, WN, WK, MT, NT, BK},
+    TDI8_CONFIG_LIST(TDI8_DESC)
+#undef TDI8_DESC
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+StaticCfg static_cfg(int id) {
+    const Desc &d = kDesc[id];
+    StaticCfg s{};
+    s.id = d.id;
+    s.family = d.family;
+    s.mf = d.mf;
+    s.wm = d.wm;
+    s.wn = d.wn;
+    s.wk = d.wk;
+    s.mt = d.mt;
+    s.nt = d.nt;
+    s.bk = d.bk;
+    s.block_m_threads = d.wm * d.mf;
+    s.block_n_threads = d.wn * d.mf;
+    s.bm = s.block_m_threads * d.mt;
+    s.bn = s.block_n_threads * d.nt;
+    s.threads = 64 * d.wm * d.wn * d.wk;
+    s.mfma_k = d.mf == 32 ? 32 : 64;
+    s.lds_bytes = d.family == 0 ? 2 * (s.bm + s.bn) * d.bk : d.wk * d.mt * d.nt * 64 * 16;
+    s.reuse1_id = -1;
+    for (const Desc &e : kDesc) {
+        if (e.family == d.family && e.mf == d.mf && e.wm == d.wm && e.wn == d.wn && e.wk == d.wk &&
+            e.bk == d.bk && e.mt == 1 && e.nt == 1) {
+            s.reuse1_id = e.id;
+            break;
+        }
+    }
+    return s;
+}
+
+namespace {
+
+struct Cand {
+    StaticCfg c;
+    int bpc;
+};
+
+int64_t thread_blocks(const StaticCfg &c, int64_t M, int64_t N) { return cdiv(M, c.bm) * cdiv(N, c.bn); }
+
+bool passes_step2(const StaticCfg &c, int bpc, const tdi8_hw_info &hw) {
+    const bool split = c.block_m_threads % c.mf == 0 && c.block_n_threads % c.mf == 0 &&
+                       c.block_m_threads >= 16 && c.block_n_threads >= 16 &&
+                       c.threads <= hw.max_threads_per_block;
+    return split && bpc >= 1 && static_cast<int64_t>(bpc) * c.threads >= hw.min_active_threads;
+}
+
+// Sign of ratio(a) - ratio(b) with ratio = BM*BN/(BM+BN).
+int compare_ratio(const StaticCfg &a, const StaticCfg &b) {
+    const int64_t l = static_cast<int64_t>(a.bm) * a.bn * (b.bm + b.bn);
+    const int64_t r = static_cast<int64_t>(b.bm) * b.bn * (a.bm + a.bn);
+    return (l > r) - (l < r);
+}
+
+}  // namespace
+
+int select_config(int M, int N, int K, const tdi8_hw_info &hw, const int *bpc, tdi8_selection *out) {
+    (void)K;  // the claims select on (m, n) only
+    Cand list[TDI8_NUM_CONFIGS];
+    int count[5] = {0, 0, 0, 0, 0};
+
+    // Steps 1 and 2.
+    Cand s2[TDI8_NUM_CONFIGS];
+    int n2 = 0;
+    for (int id = 0; id < TDI8_NUM_CONFIGS; ++id) {
+        const StaticCfg c = static_cfg(id);
+        if (c.family != 0) continue;
+        ++count[0];
+        if (passes_step2(c, bpc[id], hw)) s2[n2++] = Cand{c, bpc[id]};
+    }
+    count[1] = n2;
+    if (n2 == 0) return TDI8_ERR_BAD_CONFIG;
+
+    // Step 3.
+    int n3 = 0;
+    int route = TDI8_ROUTE_GENERAL;
+    for (int i = 0; i < n2; ++i)
+        if (thread_blocks(s2[i].c, M, N) >= static_cast<int64_t>(hw.num_cu) * s2[i].bpc) list[n3++] = s2[i];
+    if (n3 == 0) {
+        route = TDI8_ROUTE_FALLBACK;
+        bool taken[TDI8_NUM_CONFIGS] = {};
+        for (int i = 0; i < n2; ++i) {
+            const int r = s2[i].c.reuse1_id;
+            if (r >= 0 && !taken[r] && passes_step2(static_cfg(r), bpc[r], hw)) taken[r] = true;
+        }
+        for (int id = 0; id < TDI8_NUM_CONFIGS; ++id)
+            if (taken[id]) list[n3++] = Cand{static_cfg(id), bpc[id]};
+        if (M <= hw.skinny_max_m) {
+            int best_bm = 0;
+            for (int id = 0; id < TDI8_NUM_CONFIGS; ++id) {
+                const StaticCfg c = static_cfg(id);
+                if (c.family == 1 && c.bm >= M && passes_step2(c, bpc[id], hw) && (best_bm == 0 || c.bm < best_bm))
+                    best_bm = c.bm;
+            }
+            if (best_bm > 0) {
+                route = TDI8_ROUTE_SKINNY;
+                Cand sk[TDI8_NUM_CONFIGS];
+                int nsk = 0, nfill = 0;
+                for (int id = 0; id < TDI8_NUM_CONFIGS; ++id) {
+                    const StaticCfg c = static_cfg(id);
+                    if (c.family == 1 && c.bm == best_bm && passes_step2(c, bpc[id], hw)) sk[nsk++] = Cand{c, bpc[id]};
+                }
+                for (int i = 0; i < nsk; ++i)
+                    if (thread_blocks(sk[i].c, M, N) >= hw.num_cu) list[nfill++] = sk[i];
+                if (nfill == 0)
+                    for (int i = 0; i < nsk; ++i) list[nfill++] = sk[i];
+                n3 = nfill;
+            }
+        }
+    }
+    count[2] = n3;
+
+    // Step 4: all candidates tied at the largest ratio, in table order.
+    int best = 0;
+    for (int i = 1; i < n3; ++i)
+        if (compare_ratio(list[i].c, list[best].c) > 0) best = i;
+    Cand s4[TDI8_NUM_CONFIGS];
+    int n4 = 0;
+    for (int i = 0; i < n3; ++i)
+        if (compare_ratio(list[i].c, list[best].c) == 0) s4[n4++] = list[i];
+    count[3] = n4;
+
+    // Step 5.
+    int64_t fewest = -1;
+    for (int i = 0; i < n4; ++i) {
+        const int64_t rounds = cdiv(thread_blocks(s4[i].c, M, N), static_cast<int64_t>(hw.num_cu) * s4[i].bpc);
+        if (fewest < 0 || rounds < fewest) fewest = rounds;
+    }
+    int pick = -1;
+    for (int i = 0; i < n4; ++i) {
+        const int64_t rounds = cdiv(thread_blocks(s4[i].c, M, N), static_cast<int64_t>(hw.num_cu) * s4[i].bpc);
+        if (rounds == fewest) {
+            ++count[4];
+            if (pick < 0) pick = s4[i].c.id;
+        }
+    }
+    if (out) {
+        out->id = pick;
+        out->route = route;
+        for (int i = 0; i < 5; ++i) out->survivors[i] = count[i];
+    }
+    return pick;
+}
+
+}  // namespace tdi8

@@ -1,0 +1,24 @@
+// Host-side selection of a tile configuration (no HIP dependency).
+#pragma once
+
+#include "../../include/tdi8.h"
+#include "configs.h"
+
+namespace tdi8 {
+
+// Static parameters of one configuration, derived from the configuration list.
+struct StaticCfg {
+    int id, family, mf, wm, wn, wk, mt, nt, bk;
+    int block_m_threads, block_n_threads;  // the claims' thread split along M and N
+    int bm, bn;                            // block tile
+    int threads, mfma_k, lds_bytes;
+    int reuse1_id;                         // same split with m_tiles = n_tiles = 1, or -1
+};
+
+StaticCfg static_cfg(int id);
+
+// The selection on described hardware; bpc[id] = resident blocks per compute
+// unit of configuration id.  Returns the id, or a negative status.
+int select_config(int M, int N, int K, const tdi8_hw_info &hw, const int *bpc, tdi8_selection *out);
+
+}  // namespace tdi8

@@ -1,0 +1,266 @@
+// General tiled int8 GEMM kernel for gfx950 (CDNA4), one instantiation per
+// tile configuration.
+//
+// Block tile BM x BN of C, K walked in BK-deep tiles staged through LDS:
+//  * tiling of global -> LDS -> registers cuts the re-reads of A and B by
+//    the block and register tile sizes ("CUDA编程实践", section 3, the
+//    global->shared and shared->register tiling paragraphs);
+//  * two LDS stages: the next K tile is fetched into registers while the
+//    current one is consumed, then written to the other stage, one barrier
+//    per K tile (same section, the data-prefetch = double-buffer paragraph);
+//  * 16-byte chunks of each LDS row are XOR-permuted by row so that the 16
+//    lanes of a matrix-core operand read, which hit 16 consecutive rows at
+//    one chunk column, touch 16 distinct 16-byte bank groups (the padding
+//    idea of the contest write-up's "Padding 解决 bankconflict" section and
+//    of the tutorial's section 1.3/1.4, done as a permutation so no LDS is
+//    spent on padding);
+//  * the contraction runs on the int8 matrix cores:
+//    v_mfma_i32_32x32x32_i8 (MF = 32) or v_mfma_i32_16x16x64_i8 (MF = 16),
+//    each wave owning MT x NT instruction tiles (register tiling; MT, NT are
+//    the patent's m_tiles / n_tiles).
+//
+// Operand order.  The instruction computes D = X * Y with X's rows and Y's
+// columns spread over lanes and the K values of an operand held 16 per lane.
+// Both of our LDS tiles are K-contiguous (A as [BM][BK], B as [BN][BK]), so
+// either can play X.  B plays X and A plays Y: D[n][m] = C[m][n], and the
+// accumulator layout then gives each lane four consecutive n of one row m of
+// C, which is one 16-byte store into row-major C with no LDS round trip.
+//
+// B layouts.  Column-major B (N x K, K contiguous) is staged like A.
+// Row-major B (K x N, N contiguous) is fetched as 16 (k) x 4 (n) byte blocks
+// with dword loads, transposed in registers, and written K-contiguous.
+//
+// FAST = true: no predication; the dispatcher guarantees M % BM == 0,
+// N % BN == 0, K % BK == 0, 16-byte aligned A, B, C and lda, ldb multiples
+// of 16 (ldb of 4 for row-major B) and ldc of 4.  FAST = false: every load
+// is bounded by M, N, K and any alignment is accepted; bytes past K read as
+// zero, so the padded part of the last K tile adds exactly 0.
+#pragma once
+
+#include "device_common.h"
+
+namespace tdi8 {
+
+// Permutation of the 16-byte chunks of LDS row r (CPR chunks per row).
+template <int CPR>
+__device__ __forceinline__ int chunk_swizzle(int r) {
+    static_assert(CPR == 4 || CPR == 8, "BK must be 64 or 128");
+    if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
+    else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+}
+
+template <int MF>
+struct Mfma;
+
+template <>
+struct Mfma<32> {
+    using Acc = i32x16;
+    static constexpr int KSTEP = 32;  // K per instruction
+    static __device__ __forceinline__ Acc run(i32x4 x, i32x4 y, Acc c) {
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(x, y, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mfma<16> {
+    using Acc = i32x4;
+    static constexpr int KSTEP = 64;
+    static __device__ __forceinline__ Acc run(i32x4 x, i32x4 y, Acc c) {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(x, y, c, 0, 0, 0);
+    }
+};
+
+template <int MF, int WM, int WN, int MT, int NT, int BK, bool BCOL, bool FAST>
+__global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(GemmArgs g) {
+    constexpr int NTH = WM * WN * 64;
+    constexpr int BM = WM * MF * MT;
+    constexpr int BN = WN * MF * NT;
+    constexpr int CPR = BK / 16;                  // 16-byte chunks per LDS row
+    constexpr int A_BYTES = BM * BK;
+    constexpr int STAGE = (BM + BN) * BK;
+    constexpr int A_CHUNKS = BM * CPR;
+    constexpr int B_CHUNKS = BN * CPR;
+    constexpr int A_PER = (A_CHUNKS + NTH - 1) / NTH;
+    constexpr int B_PER = (B_CHUNKS + NTH - 1) / NTH;
+    constexpr int RR_BLOCKS = (BK / 16) * (BN / 4);    // 16x4 byte blocks of row-major B
+    constexpr int RR_PER = (RR_BLOCKS + NTH - 1) / NTH;
+    constexpr int KSTEPS = BK / Mfma<MF>::KSTEP;
+    using Acc = typename Mfma<MF>::Acc;
+
+    __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+    const int tm = blockIdx.x / g.tiles_n;
+    const int tn = blockIdx.x % g.tiles_n;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+
+    Acc acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = Acc{};
+
+    i32x4 ra[A_PER];
+    i32x4 rb[BCOL ? B_PER : 1];
+    uint32_t rw[BCOL ? 1 : RR_PER * 16];
+
+    // Global -> registers for K tile starting at k0.
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) {
+            const int q = tid + i * NTH;
+            if (A_CHUNKS % NTH == 0 || q < A_CHUNKS) {
+                const int r = q / CPR;
+                const int c = (q % CPR) ^ chunk_swizzle<CPR>(r);
+                const int row = m0 + r;
+                const int kk = k0 + 16 * c;
+                const int8_t *p = g.A + static_cast<int64_t>(row) * g.lda + kk;
+                ra[i] = FAST ? load16(p) : load16_masked(p, row < g.M ? clamp16(g.K - kk) : 0);
+            }
+        }
+        if constexpr (BCOL) {
+#pragma unroll
+            for (int i = 0; i < B_PER; ++i) {
+                const int q = tid + i * NTH;
+                if (B_CHUNKS % NTH == 0 || q < B_CHUNKS) {
+                    const int r = q / CPR;
+                    const int c = (q % CPR) ^ chunk_swizzle<CPR>(r);
+                    const int col = n0 + r;
+                    const int kk = k0 + 16 * c;
+                    const int8_t *p = g.B + static_cast<int64_t>(col) * g.ldb + kk;
+                    rb[i] = FAST ? load16(p) : load16_masked(p, col < g.N ? clamp16(g.K - kk) : 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RR_PER; ++i) {
+                const int u = tid + i * NTH;
+                if (RR_BLOCKS % NTH == 0 || u < RR_BLOCKS) {
+                    const int nb = u % (BN / 4);
+                    const int kq = u / (BN / 4);
+                    const int col = n0 + 4 * nb;
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) {
+                        const int k = k0 + 16 * kq + t;
+                        const int8_t *p = g.B + static_cast<int64_t>(k) * g.ldb + col;
+                        rw[i * 16 + t] = FAST ? *reinterpret_cast<const uint32_t *>(p)
+                                              : load4_masked(p, k < g.K ? clamp4(g.N - col) : 0);
+                    }
+                }
+            }
+        }
+    };
+
+    // Registers -> LDS stage s.
+    auto stash = [&](int s) {
+        int8_t *base = lds + s * STAGE;
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) {
+            const int q = tid + i * NTH;
+            if (A_CHUNKS % NTH == 0 || q < A_CHUNKS)
+                *reinterpret_cast<i32x4 *>(base + 16 * q) = ra[i];
+        }
+        if constexpr (BCOL) {
+#pragma unroll
+            for (int i = 0; i < B_PER; ++i) {
+                const int q = tid + i * NTH;
+                if (B_CHUNKS % NTH == 0 || q < B_CHUNKS)
+                    *reinterpret_cast<i32x4 *>(base + A_BYTES + 16 * q) = rb[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RR_PER; ++i) {
+                const int u = tid + i * NTH;
+                if (RR_BLOCKS % NTH == 0 || u < RR_BLOCKS) {
+                    const int nb = u % (BN / 4);
+                    const int kq = u / (BN / 4);
+                    uint32_t t4[4][4];  // [k quad][column]
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) transpose4x4(&rw[i * 16 + 4 * qd], t4[qd]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 4 * nb + j;
+                        const int c = kq ^ chunk_swizzle<CPR>(r);
+                        i32x4 v;
+                        v[0] = static_cast<int32_t>(t4[0][j]);
+                        v[1] = static_cast<int32_t>(t4[1][j]);
+                        v[2] = static_cast<int32_t>(t4[2][j]);
+                        v[3] = static_cast<int32_t>(t4[3][j]);
+                        *reinterpret_cast<i32x4 *>(base + A_BYTES + r * BK + 16 * c) = v;
+                    }
+                }
+            }
+        }
+    };
+
+    // Matrix-core work on LDS stage s.
+    auto compute = [&](int s) {
+        const int8_t *As = lds + s * STAGE;
+        const int8_t *Bs = As + A_BYTES;
+        const int lrow = lane % MF;
+        const int lgrp = lane / MF;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const int c = ks * (Mfma<MF>::KSTEP / 16) + lgrp;
+            i32x4 xa[MT], xb[NT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const int r = wm * (MT * MF) + i * MF + lrow;
+                xa[i] = *reinterpret_cast<const i32x4 *>(As + r * BK + 16 * (c ^ chunk_swizzle<CPR>(r)));
+            }
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int r = wn * (NT * MF) + j * MF + lrow;
+                xb[j] = *reinterpret_cast<const i32x4 *>(Bs + r * BK + 16 * (c ^ chunk_swizzle<CPR>(r)));
+            }
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) acc[i][j] = Mfma<MF>::run(xb[j], xa[i], acc[i][j]);
+        }
+    };
+
+    const int nk = (g.K + BK - 1) / BK;
+    if (nk > 0) {
+        fetch(0);
+        stash(0);
+        __syncthreads();
+        for (int t = 0; t < nk; ++t) {
+            if (t + 1 < nk) fetch((t + 1) * BK);
+            compute(t & 1);
+            if (t + 1 < nk) stash((t + 1) & 1);
+            __syncthreads();
+        }
+    }
+
+    // Epilogue: lane holds D[n][m] = C[m][n] with four consecutive n per
+    // group of four accumulator registers.
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int mb = m0 + wm * (MT * MF) + i * MF;
+            const int nbase = n0 + wn * (NT * MF) + j * MF;
+            if constexpr (MF == 32) {
+                const int m = mb + (lane & 31);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = nbase + 8 * q + 4 * (lane >> 5);
+                    i32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    store4<FAST>(g, m, n, v);
+                }
+            } else {
+                const int m = mb + (lane & 15);
+                const int n = nbase + 4 * (lane >> 4);
+                store4<FAST>(g, m, n, acc[i][j]);
+            }
+        }
+    }
+}
+
+}  // namespace tdi8
