@@ -114,8 +114,9 @@ typedef struct {
     int waves_m, waves_n, waves_k;
     int m_tiles, n_tiles;        /* per-wave instruction repeats (the claims' data reuse) */
     int block_m, block_n, block_k;
+    int stages;          /* LDS stages of the unpredicated column-major-B kernel */
     int threads;
-    int lds_bytes;       /* static LDS per block */
+    int lds_bytes;       /* static LDS per block of that kernel */
     int vgprs, agprs;    /* per lane, from the compiled kernel (0 before a device is seen) */
     int blocks_per_cu;   /* resident blocks per compute unit, from the occupancy query */
     int reuse1_id;       /* configuration with the same thread split and m_tiles = n_tiles = 1 */

@@ -94,10 +94,12 @@ def test_config_table_shape():
         assert c.threads == 64 * c.waves_m * c.waves_n * c.waves_k
         assert c.mfma_k == (32 if c.mfma_m == 32 else 64)
         sib = tab[c.reuse1_id]
-        assert (sib.family, sib.mfma_m, sib.waves_m, sib.waves_n, sib.waves_k, sib.block_k, sib.m_tiles,
-                sib.n_tiles) == (c.family, c.mfma_m, c.waves_m, c.waves_n, c.waves_k, c.block_k, 1, 1)
+        assert (sib.family, sib.mfma_m, sib.waves_m, sib.waves_n, sib.waves_k, sib.block_k, sib.stages,
+                sib.m_tiles, sib.n_tiles) == (c.family, c.mfma_m, c.waves_m, c.waves_n, c.waves_k, c.block_k,
+                                              c.stages, 1, 1)
         if c.family == 0:
-            assert c.lds_bytes == 2 * (c.block_m + c.block_n) * c.block_k <= 160 * 1024
+            assert c.lds_bytes == c.stages * (c.block_m + c.block_n) * c.block_k <= 160 * 1024
+            assert c.stages >= 2 and (c.block_k // (32 if c.mfma_m == 32 else 64)) % 2 == 0
     assert any(c.family == 1 and c.block_m == 16 for c in tab)
     assert any(c.family == 1 and c.block_m == 32 for c in tab)
 
@@ -105,7 +107,7 @@ def test_config_table_shape():
 def oracle_table(bpc):
     fam = {0: "general", 1: "skinny"}
     return [Cfg(c.id, fam[c.family], c.mfma_m, c.mfma_n, c.waves_m, c.waves_n, c.m_tiles, c.n_tiles,
-                c.block_k, c.threads, bpc[c.id]) for c in library_table()]
+                c.block_k, c.threads, bpc[c.id], c.stages) for c in library_table()]
 
 
 def fake_bpc(lds_per_cu=160 * 1024, waves_per_cu=32):
@@ -120,7 +122,7 @@ def fake_bpc(lds_per_cu=160 * 1024, waves_per_cu=32):
 
 HARDWARE = [
     (Hw(256, 1024, 256, 32), fake_bpc()),
-    (Hw(256, 1024, 256, 32), [1] * 15),
+    (Hw(256, 1024, 256, 32), [1] * 64),
     (Hw(304, 1024, 256, 32), fake_bpc(64 * 1024)),
     (Hw(80, 256, 128, 16), fake_bpc(64 * 1024, 16)),
     (Hw(256, 1024, 1024, 32), fake_bpc()),

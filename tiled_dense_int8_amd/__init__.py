@@ -37,7 +37,7 @@ ROUTE_GENERAL, ROUTE_FALLBACK, ROUTE_SKINNY = 0, 1, 2
 class TileConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "id", "family", "mfma_m", "mfma_n", "mfma_k", "waves_m", "waves_n", "waves_k",
-        "m_tiles", "n_tiles", "block_m", "block_n", "block_k", "threads", "lds_bytes",
+        "m_tiles", "n_tiles", "block_m", "block_n", "block_k", "stages", "threads", "lds_bytes",
         "vgprs", "agprs", "blocks_per_cu", "reuse1_id")]
 
     def as_dict(self) -> dict:

@@ -41,27 +41,32 @@ def _run(cmd: list[str]) -> None:
         raise RuntimeError("hipcc failed: " + " ".join(cmd[-3:]))
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, verbose: bool = False, extra_flags: list[str] | None = None,
+          out: str | None = None, build_dir: str | None = None) -> str:
+    """Compile every configuration and link the library (default: in-tree libtdi8.so)."""
+    out = out or LIB
+    bdir = build_dir or BUILD
+    flags = FLAGS + list(extra_flags or [])
+    os.makedirs(bdir, exist_ok=True)
     jobs = jobs or min(16, os.cpu_count() or 4)
     units = []
     for cid in config_ids():
-        obj = os.path.join(BUILD, f"cfg{cid}.o")
-        units.append([HIPCC, *FLAGS, f"-DTDI8_CFG={cid}", "-c",
+        obj = os.path.join(bdir, f"cfg{cid}.o")
+        units.append([HIPCC, *flags, f"-DTDI8_CFG={cid}", "-c",
                       os.path.join(CSRC, "instantiate.hip"), "-o", obj])
-    units.append([HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, "abi.cpp"),
-                  "-o", os.path.join(BUILD, "abi.o")])
-    units.append([HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, "selector.cpp"),
-                  "-o", os.path.join(BUILD, "selector.o")])
+    units.append([HIPCC, *flags, "-x", "hip", "-c", os.path.join(CSRC, "abi.cpp"),
+                  "-o", os.path.join(bdir, "abi.o")])
+    units.append([HIPCC, *flags, "-x", "hip", "-c", os.path.join(CSRC, "selector.cpp"),
+                  "-o", os.path.join(bdir, "selector.o")])
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(_run, units))
     objs = [u[u.index("-o") + 1] for u in units]
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -257,6 +257,7 @@ int tile_config_info(int id, tdi8_tile_config *out) {
     t.block_m = c.bm;
     t.block_n = c.bn;
     t.block_k = c.bk;
+    t.stages = c.stages;
     t.threads = c.threads;
     t.lds_bytes = c.lds_bytes;
     t.reuse1_id = c.reuse1_id;

@@ -3,35 +3,41 @@
 // kernel, every configuration is compiled, and the run-time selection picks
 // one.  Claim 1 step 1 enumerates exactly this list.
 //
-// X(id, family, MF, WM, WN, WK, MT, NT, BK)
+// X(id, family, MF, WM, WN, WK, MT, NT, BK, ST)
 //   family  0 = general tiled kernel, 1 = skinny kernel (K split across waves)
 //   MF      matrix-core tile: 32 -> v_mfma_i32_32x32x32_i8, 16 -> v_mfma_i32_16x16x64_i8
 //   WM, WN  waves of the block along M and N (general family; 1 for skinny)
 //   WK      waves of the block along K (skinny family; 1 for general)
 //   MT, NT  instruction tiles per wave along M and N (the claims' m_tiles, n_tiles)
 //   BK      K depth of one LDS stage (general) or of one wave step (skinny)
+//   ST      LDS stages of the pipelined column-major-B kernel (general)
 // Block tile: BM = WM*MF*MT rows of C, BN = WN*MF*NT columns.
 //
-// Every general entry has its reuse-1 sibling (same MF, WM, WN, BK with
+// Every general entry has its reuse-1 sibling (same MF, WM, WN, BK, ST with
 // MT = NT = 1) in the list, as the fill step's fallback needs.
 #pragma once
 
-#define TDI8_CONFIG_LIST(X)                                   \
-    X(0, 0, 32, 2, 2, 1, 4, 4, 128)  /* 256 x 256, 4 waves */  \
-    X(1, 0, 32, 2, 2, 1, 2, 4, 128)  /* 128 x 256, 4 waves */  \
-    X(2, 0, 32, 2, 2, 1, 2, 2, 128)  /* 128 x 128, 4 waves */  \
-    X(3, 0, 32, 2, 2, 1, 2, 1, 128)  /* 128 x  64, 4 waves */  \
-    X(4, 0, 32, 2, 2, 1, 1, 1, 128)  /*  64 x  64, reuse 1 */  \
-    X(5, 0, 32, 2, 4, 1, 4, 2, 128)  /* 256 x 256, 8 waves */  \
-    X(6, 0, 32, 2, 4, 1, 1, 1, 128)  /*  64 x 128, reuse 1 */  \
-    X(7, 0, 16, 2, 2, 1, 4, 4, 128)  /* 128 x 128, 4 waves */  \
-    X(8, 0, 16, 2, 2, 1, 2, 2, 128)  /*  64 x  64, 4 waves */  \
-    X(9, 0, 16, 2, 2, 1, 1, 1, 128)  /*  32 x  32, reuse 1 */  \
-    X(10, 1, 16, 1, 1, 8, 1, 1, 256) /* skinny 16 x 16, 8 K-waves */  \
-    X(11, 1, 16, 1, 1, 16, 1, 1, 256) /* skinny 16 x 16, 16 K-waves */ \
-    X(12, 1, 16, 1, 1, 8, 1, 2, 256) /* skinny 16 x 32, 8 K-waves */  \
-    X(13, 1, 16, 1, 1, 8, 2, 1, 256) /* skinny 32 x 16, 8 K-waves */  \
-    X(14, 1, 16, 1, 1, 8, 2, 2, 256) /* skinny 32 x 32, 8 K-waves */
+#define TDI8_CONFIG_LIST(X)                                          \
+    X(0, 0, 32, 2, 2, 1, 4, 4, 64, 4)   /* 256 x 256, 4 waves */     \
+    X(1, 0, 32, 2, 2, 1, 2, 4, 64, 4)   /* 128 x 256, 4 waves */     \
+    X(2, 0, 32, 2, 2, 1, 4, 2, 64, 4)   /* 256 x 128, 4 waves */     \
+    X(3, 0, 32, 2, 2, 1, 2, 2, 64, 4)   /* 128 x 128, 4 waves */     \
+    X(4, 0, 32, 2, 2, 1, 2, 1, 64, 4)   /* 128 x  64, 4 waves */     \
+    X(5, 0, 32, 2, 2, 1, 1, 1, 64, 4)   /*  64 x  64, reuse 1 */     \
+    X(6, 0, 32, 2, 4, 1, 4, 2, 128, 2)  /* 256 x 256, 8 waves */     \
+    X(7, 0, 32, 2, 4, 1, 1, 1, 128, 2)  /*  64 x 128, reuse 1 */     \
+    X(8, 0, 32, 4, 2, 1, 2, 4, 128, 2)  /* 256 x 256, 8 waves */     \
+    X(9, 0, 32, 4, 2, 1, 1, 1, 128, 2)  /* 128 x  64, reuse 1 */     \
+    X(10, 0, 32, 2, 2, 1, 4, 4, 128, 2) /* 256 x 256, BK 128 */      \
+    X(11, 0, 32, 2, 2, 1, 1, 1, 128, 2) /*  64 x  64, reuse 1 */     \
+    X(12, 0, 16, 2, 2, 1, 4, 4, 128, 2) /* 128 x 128, 16x16 tiles */ \
+    X(13, 0, 16, 2, 2, 1, 2, 2, 128, 2) /*  64 x  64 */              \
+    X(14, 0, 16, 2, 2, 1, 1, 1, 128, 2) /*  32 x  32, reuse 1 */     \
+    X(15, 1, 16, 1, 1, 8, 1, 1, 256, 1)  /* skinny 16 x 16, 8 K-waves */  \
+    X(16, 1, 16, 1, 1, 16, 1, 1, 256, 1) /* skinny 16 x 16, 16 K-waves */ \
+    X(17, 1, 16, 1, 1, 8, 1, 2, 256, 1)  /* skinny 16 x 32, 8 K-waves */  \
+    X(18, 1, 16, 1, 1, 8, 2, 1, 256, 1)  /* skinny 32 x 16, 8 K-waves */  \
+    X(19, 1, 16, 1, 1, 8, 2, 2, 256, 1)  /* skinny 32 x 32, 8 K-waves */
 
 #define TDI8_COUNT_ONE(...) +1
 enum { TDI8_NUM_CONFIGS = 0 TDI8_CONFIG_LIST(TDI8_COUNT_ONE) };

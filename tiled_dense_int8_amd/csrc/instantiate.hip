@@ -3,6 +3,7 @@
 // points.  Patent application CN114238853A, claim 7: every configuration's
 // parameters become the kernel's template parameters and all are compiled.
 #include "kernel_table.h"
+#include "rc_pipelined_kernel.h"
 #include "skinny_kernel.h"
 #include "tiled_kernel.h"
 
@@ -17,7 +18,10 @@ namespace tdi8 {
 
 template <class P, bool BCOL, bool FAST>
 static const void *entry() {
-    if constexpr (P::family == 0)
+    if constexpr (P::family == 0 && BCOL && FAST)
+        return reinterpret_cast<const void *>(
+            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, P::st>);
+    else if constexpr (P::family == 0)
         return reinterpret_cast<const void *>(
             &gemm_tiled_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, BCOL, FAST>);
     else if constexpr (BCOL)

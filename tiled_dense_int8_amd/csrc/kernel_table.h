@@ -9,11 +9,11 @@ namespace tdi8 {
 template <int ID>
 struct CfgParams;
 
-#define TDI8_DEFINE_PARAMS(ID, FAM, MF_, WM_, WN_, WK_, MT_, NT_, BK_)                   \
+#define TDI8_DEFINE_PARAMS(ID, FAM, MF_, WM_, WN_, WK_, MT_, NT_, BK_, ST_)              \
     template <>                                                                          \
     struct CfgParams<ID> {                                                               \
         static constexpr int family = FAM, mf = MF_, wm = WM_, wn = WN_, wk = WK_,       \
-                             mt = MT_, nt = NT_, bk = BK_;                               \
+                             mt = MT_, nt = NT_, bk = BK_, st = ST_;                     \
     };
 TDI8_CONFIG_LIST(TDI8_DEFINE_PARAMS)
 #undef TDI8_DEFINE_PARAMS

@@ -1,0 +1,278 @@
+// Unpredicated int8 GEMM kernel for column-major B on gfx950: the form the
+// dispatcher uses when every dimension is a tile multiple and the operands
+// are 16-byte aligned (A row-major and B column-major are then both
+// K-contiguous, so both tiles can go from HBM to LDS with no register
+// staging).
+//
+// Differences from gemm_tiled_kernel:
+//  * global -> LDS with global_load_lds_dwordx4: each wave instruction moves
+//    1 KiB straight into LDS (lane l's 16 bytes land at l*16 of the block),
+//    so no VGPRs hold staged tiles and no ds_write is issued;
+//  * STAGES LDS buffers; loads run STAGES-1 K tiles ahead, and one barrier
+//    per K tile both publishes the next tile and retires the oldest buffer
+//    (prefetch = double buffering generalised; "CUDA编程实践" section 3, the
+//    data-prefetch paragraph);
+//  * instruction operands are prefetched one K step ahead in registers; the
+//    first step of the next K tile is read right after the barrier, under
+//    the last step's matrix-core work;
+//  * blocks are ordered so that the blocks resident on one XCD (workgroups
+//    are dealt to the 8 XCDs round-robin) cover a compact group of tiles
+//    and share A and B rows in that XCD's L2 (the contest write-up's
+//    "Swizzle 线程块映射" idea; its point that flat waves of blocks lose L2
+//    reuse is the "矩阵维度高度不均衡" paragraph).
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "tiled_kernel.h"
+
+namespace tdi8 {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+#define TDI8_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14))
+// s_waitcnt lgkmcnt(0) with the other counters left at max.
+#define TDI8_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (3 << 14))
+
+// Tile coordinates of block `bid` in XCD-grouped order.
+__device__ __forceinline__ void tile_of_block(const GemmArgs &g, int bid, int &tm, int &tn) {
+    const int total = g.tiles_m * g.tiles_n;
+    int l = bid;
+    if ((total & 7) == 0) l = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int group_rows = 4;
+    const int gsize = group_rows * g.tiles_n;
+    const int first = (l / gsize) * group_rows;
+    const int rows = min(g.tiles_m - first, group_rows);
+    const int within = l % gsize;
+    tm = first + within % rows;
+    tn = within / rows;
+}
+
+template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES>
+__global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArgs g) {
+    constexpr int NW = WM * WN;
+    constexpr int BM = WM * MF * MT;
+    constexpr int BN = WN * MF * NT;
+    constexpr int CPR = BK / 16;
+    constexpr int A_CHUNKS = BM * CPR;
+    constexpr int STAGE = (BM + BN) * BK;
+    constexpr int LOADS = STAGE / 1024;          // 1 KiB wave instructions per stage
+    constexpr int LPW = LOADS / NW;              // per wave
+    constexpr int KSTEP = Mfma<MF>::KSTEP;
+    constexpr int KS = BK / KSTEP;
+    constexpr int KC = KSTEP / 16;               // 16-byte chunks per lane group per step
+    static_assert(LOADS % NW == 0, "stage must split evenly over the waves");
+    static_assert(A_CHUNKS % 64 == 0, "A region must be whole wave instructions");
+    static_assert(STAGES >= 2, "at least two stages");
+    static_assert(KS % 2 == 0, "operand double buffer needs an even number of K steps per tile");
+    using Acc = typename Mfma<MF>::Acc;
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+
+    __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * STAGE];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+    int tm, tn;
+    tile_of_block(g, blockIdx.x, tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int nk = g.K / BK;
+
+    // Per-lane source pointers of this wave's load instructions (K offset 0).
+    const int8_t *src[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int q = (i * NW + wave) * 64 + lane;
+        if (q < A_CHUNKS) {
+            const int r = q / CPR;
+            const int c = (q % CPR) ^ chunk_swizzle<CPR>(r);
+            src[i] = g.A + static_cast<int64_t>(m0 + r) * g.lda + 16 * c;
+        } else {
+            const int qb = q - A_CHUNKS;
+            const int r = qb / CPR;
+            const int c = (qb % CPR) ^ chunk_swizzle<CPR>(r);
+            src[i] = g.B + static_cast<int64_t>(n0 + r) * g.ldb + 16 * c;
+        }
+    }
+    auto issue_one = [&](int kt, int i) {
+        int8_t *dst = lds + (kt % STAGES) * STAGE + (i * NW + wave) * 1024;
+        __builtin_amdgcn_global_load_lds(src[i] + kt * BK, (lds_void_t *)dst, 16, 0, 0);
+    };
+    auto issue = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) issue_one(kt, i);
+    };
+
+    // LDS byte offsets (within a stage) of this lane's operand rows.
+    const int lrow = lane % MF;
+    const int lgrp = lane / MF;
+    int offa[MT], offb[NT], swa[MT], swb[NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int r = wm * (MT * MF) + i * MF + lrow;
+        offa[i] = r * BK;
+        swa[i] = chunk_swizzle<CPR>(r);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int r = BM + wn * (NT * MF) + j * MF + lrow;
+        offb[j] = r * BK;
+        swb[j] = chunk_swizzle<CPR>(r - BM);
+    }
+
+    Acc acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = Acc{};
+
+    i32x4 fa[2][MT], fb[2][NT];
+    auto read_one = [&](int kt, int ks, int buf, int r) {
+        const int8_t *base = lds + (kt % STAGES) * STAGE;
+        const int c = ks * KC + lgrp;
+        if (r < MT)
+            fa[buf][r] = *reinterpret_cast<const i32x4 *>(base + offa[r] + 16 * (c ^ swa[r]));
+        else
+            fb[buf][r - MT] = *reinterpret_cast<const i32x4 *>(base + offb[r - MT] + 16 * (c ^ swb[r - MT]));
+    };
+    auto read_frags = [&](int kt, int ks, int buf) {
+        const int8_t *base = lds + (kt % STAGES) * STAGE;
+        const int c = ks * KC + lgrp;
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+            fa[buf][i] = *reinterpret_cast<const i32x4 *>(base + offa[i] + 16 * (c ^ swa[i]));
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            fb[buf][j] = *reinterpret_cast<const i32x4 *>(base + offb[j] + 16 * (c ^ swb[j]));
+    };
+    constexpr int F = MT * NT;   // matrix-core instructions per K step
+    constexpr int R = MT + NT;   // operand reads per K step
+    auto mma_one = [&](int buf, int x) {
+        const int i = x / NT, j = x % NT;
+        acc[i][j] = Mfma<MF>::run(fb[buf][j], fa[buf][i], acc[i][j]);
+    };
+    constexpr int NS = (KS - 1) * F;  // matrix-core slots before the last K step
+
+    // One K tile, as a fixed instruction order (each matrix-core instruction
+    // followed by the memory operations slotted after it, fenced so the
+    // compiler keeps the order):
+    //  * K steps 0 .. KS-2: after matrix instruction x of step ks, the read
+    //    of operand x of step ks+1 (reads front-loaded, so they land before
+    //    the step ends), and the DMA loads of the refill of the oldest
+    //    buffer spread evenly over these (KS-1)*F slots (LOAD);
+    //  * last step: half of its matrix work, then publish tile t+1 (own DMA
+    //    loads and operand reads done, then a barrier), then the other half
+    //    with tile t+1's first-step operands read after each instruction.
+    // Each step ends by retiring its operand reads, so the next step's
+    // matrix work starts with its operands in registers.
+    auto tile = [&](int t, auto load_tag, auto next_tag) {
+        constexpr bool LOAD = decltype(load_tag)::value;
+        constexpr bool NEXT = decltype(next_tag)::value;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < KS) {
+#pragma unroll
+                for (int x = 0; x < F; ++x) {
+                    mma_one(cur, x);
+                    if (x < R) read_one(t, ks + 1, cur ^ 1, x);
+                    if (x == F - 1)
+#pragma unroll
+                        for (int r = F; r < R; ++r) read_one(t, ks + 1, cur ^ 1, r);
+                    if constexpr (LOAD) {
+                        const int gx = ks * F + x;
+#pragma unroll
+                        for (int li = 0; li < LPW; ++li)
+                            if ((li * NS) / LPW == gx) issue_one(t + STAGES - 1, li);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                constexpr int H = F / 2;
+#pragma unroll
+                for (int x = 0; x < H; ++x) {
+                    mma_one(cur, x);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if constexpr (NEXT) {
+                    // Loads issued after tile t+1's: the refills of tiles
+                    // t+2 .. t+STAGES-1.
+                    if constexpr (LOAD) {
+                        TDI8_WAIT_VMCNT((STAGES - 2) * LPW);
+                    } else {
+                        TDI8_WAIT_VMCNT(0);
+                    }
+                    TDI8_WAIT_LGKM0();
+                    __builtin_amdgcn_s_barrier();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int x = H; x < F; ++x) {
+                    mma_one(cur, x);
+                    if constexpr (NEXT) {
+                        if (x - H < R) read_one(t + 1, 0, cur ^ 1, x - H);
+                        if (x == F - 1)
+#pragma unroll
+                            for (int r = F - H; r < R; ++r) read_one(t + 1, 0, cur ^ 1, r);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            TDI8_WAIT_LGKM0();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    if (nk > 0) {
+        // Prologue: tiles 0 .. STAGES-2 in flight, wait for tile 0.
+        if (nk >= STAGES - 1) {
+#pragma unroll
+            for (int s = 0; s < STAGES - 1; ++s) issue(s);
+            TDI8_WAIT_VMCNT((STAGES - 2) * LPW);
+        } else {
+            for (int s = 0; s < nk; ++s) issue(s);
+            TDI8_WAIT_VMCNT(0);
+        }
+        __builtin_amdgcn_s_barrier();
+        read_frags(0, 0, 0);
+        TDI8_WAIT_LGKM0();  // the K loop starts with no operand read pending
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Steady state: every iteration refills a buffer and has a successor.
+        int t = 0;
+        for (; t + STAGES - 1 < nk; ++t) tile(t, std::true_type{}, std::true_type{});
+        // Drain: nothing left to fetch.
+        for (; t + 1 < nk; ++t) tile(t, std::false_type{}, std::true_type{});
+        tile(t, std::false_type{}, std::false_type{});
+    }
+
+    // Epilogue: lane holds C[m][n .. n+3] per group of four accumulators.
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int mb = m0 + wm * (MT * MF) + i * MF;
+            const int nb = n0 + wn * (NT * MF) + j * MF;
+            if constexpr (MF == 32) {
+                const int m = mb + (lane & 31);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = nb + 8 * q + 4 * (lane >> 5);
+                    i32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    store4<true>(g, m, n, v);
+                }
+            } else {
+                store4<true>(g, mb + (lane & 15), nb + 4 * (lane >> 4), acc[i][j]);
+            }
+        }
+    }
+#endif
+}
+
+}  // namespace tdi8

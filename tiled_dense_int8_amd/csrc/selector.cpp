@@ -29,11 +29,11 @@ namespace tdi8 {
 namespace {
 
 struct Desc {
-    int id, family, mf, wm, wn, wk, mt, nt, bk;
+    int id, family, mf, wm, wn, wk, mt, nt, bk, st;
 };
 
 constexpr Desc kDesc[] = {
-#define TDI8_DESC(ID, FAM, MF, WM, WN, WK, MT, NT, BK) {ID, FAM, MF, WM, WN, WK, MT, NT, BK},
+#define TDI8_DESC(ID, FAM, MF, WM, WN, WK, MT, NT, BK, ST) {ID, FAM, MF, WM, WN, WK, MT, NT, BK, ST},
     TDI8_CONFIG_LIST(TDI8_DESC)
 #undef TDI8_DESC
 };
@@ -54,17 +54,18 @@ StaticCfg static_cfg(int id) {
     s.mt = d.mt;
     s.nt = d.nt;
     s.bk = d.bk;
+    s.stages = d.st;
     s.block_m_threads = d.wm * d.mf;
     s.block_n_threads = d.wn * d.mf;
     s.bm = s.block_m_threads * d.mt;
     s.bn = s.block_n_threads * d.nt;
     s.threads = 64 * d.wm * d.wn * d.wk;
     s.mfma_k = d.mf == 32 ? 32 : 64;
-    s.lds_bytes = d.family == 0 ? 2 * (s.bm + s.bn) * d.bk : d.wk * d.mt * d.nt * 64 * 16;
+    s.lds_bytes = d.family == 0 ? d.st * (s.bm + s.bn) * d.bk : d.wk * d.mt * d.nt * 64 * 16;
     s.reuse1_id = -1;
     for (const Desc &e : kDesc) {
         if (e.family == d.family && e.mf == d.mf && e.wm == d.wm && e.wn == d.wn && e.wk == d.wk &&
-            e.bk == d.bk && e.mt == 1 && e.nt == 1) {
+            e.bk == d.bk && e.st == d.st && e.mt == 1 && e.nt == 1) {
             s.reuse1_id = e.id;
             break;
         }

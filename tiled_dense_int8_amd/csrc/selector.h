@@ -8,7 +8,7 @@ namespace tdi8 {
 
 // Static parameters of one configuration, derived from the configuration list.
 struct StaticCfg {
-    int id, family, mf, wm, wn, wk, mt, nt, bk;
+    int id, family, mf, wm, wn, wk, mt, nt, bk, stages;
     int block_m_threads, block_n_threads;  // the claims' thread split along M and N
     int bm, bn;                            // block tile
     int threads, mfma_k, lds_bytes;
