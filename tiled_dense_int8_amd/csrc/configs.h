@@ -9,9 +9,14 @@
 //   WM, WN  waves of the block along M and N (general family; 1 for skinny)
 //   WK      waves of the block along K (skinny family; 1 for general)
 //   MT, NT  instruction tiles per wave along M and N (the claims' m_tiles, n_tiles)
-//   BK      K depth of one LDS stage (general) or of one wave step (skinny)
-//   ST      LDS stages of the pipelined column-major-B kernel (general)
+//   BK      K depth of one LDS stage (general), or of one LDS chunk of the
+//           unpredicated skinny kernel
+//   ST      LDS stages of the pipelined column-major-B kernel (general), or
+//           256-byte K super-steps loaded per batch by each wave (skinny)
 // Block tile: BM = WM*MF*MT rows of C, BN = WN*MF*NT columns.
+//
+// Entries that tie in the selection are taken in list order, so within a
+// shape the one measured fastest on MI355X comes first.
 //
 // Every general entry has its reuse-1 sibling (same MF, WM, WN, BK, ST with
 // MT = NT = 1) in the list, as the fill step's fallback needs.
@@ -33,11 +38,12 @@
     X(12, 0, 16, 2, 2, 1, 4, 4, 128, 2) /* 128 x 128, 16x16 tiles */ \
     X(13, 0, 16, 2, 2, 1, 2, 2, 128, 2) /*  64 x  64 */              \
     X(14, 0, 16, 2, 2, 1, 1, 1, 128, 2) /*  32 x  32, reuse 1 */     \
-    X(15, 1, 16, 1, 1, 8, 1, 1, 256, 1)  /* skinny 16 x 16, 8 K-waves */  \
-    X(16, 1, 16, 1, 1, 16, 1, 1, 256, 1) /* skinny 16 x 16, 16 K-waves */ \
-    X(17, 1, 16, 1, 1, 8, 1, 2, 256, 1)  /* skinny 16 x 32, 8 K-waves */  \
-    X(18, 1, 16, 1, 1, 8, 2, 1, 256, 1)  /* skinny 32 x 16, 8 K-waves */  \
-    X(19, 1, 16, 1, 1, 8, 2, 2, 256, 1)  /* skinny 32 x 32, 8 K-waves */
+    X(15, 1, 16, 1, 1, 16, 1, 1, 2048, 1) /* skinny 16 x 16, 16 K-waves */ \
+    X(16, 1, 16, 1, 1, 8, 1, 1, 2048, 2)  /* skinny 16 x 16, 8 K-waves */  \
+    X(17, 1, 16, 1, 1, 4, 1, 1, 2048, 4)  /* skinny 16 x 16, 4 K-waves */  \
+    X(18, 1, 16, 1, 1, 8, 1, 2, 1024, 2)  /* skinny 16 x 32, 8 K-waves */  \
+    X(19, 1, 16, 1, 1, 8, 2, 1, 1024, 2)  /* skinny 32 x 16, 8 K-waves */  \
+    X(20, 1, 16, 1, 1, 4, 2, 2, 1024, 2)  /* skinny 32 x 32, 4 K-waves */
 
 #define TDI8_COUNT_ONE(...) +1
 enum { TDI8_NUM_CONFIGS = 0 TDI8_CONFIG_LIST(TDI8_COUNT_ONE) };

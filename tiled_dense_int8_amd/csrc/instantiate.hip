@@ -24,10 +24,12 @@ static const void *entry() {
     else if constexpr (P::family == 0)
         return reinterpret_cast<const void *>(
             &gemm_tiled_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, BCOL, FAST>);
+    else if constexpr (BCOL && FAST)
+        return reinterpret_cast<const void *>(&gemm_skinny_lds_kernel<P::mt, P::nt, P::wk, P::bk>);
     else if constexpr (BCOL)
-        return reinterpret_cast<const void *>(&gemm_skinny_kernel<P::mt, P::nt, P::wk, FAST>);
+        return reinterpret_cast<const void *>(&gemm_skinny_kernel<P::mt, P::nt, P::wk, P::st, false>);
     else
-        return reinterpret_cast<const void *>(&gemm_skinny_rr_kernel<P::mt, P::wk, FAST>);
+        return reinterpret_cast<const void *>(&gemm_skinny_rr_kernel<P::mt, P::wk, 2, FAST>);
 }
 
 void TDI8_CAT(register_cfg_, TDI8_CFG)(KernelSet *ks) {

@@ -10,13 +10,16 @@
 // splits K across its WK waves and reduces their int32 partial sums in LDS
 // (exact in any order).
 //
-// Block: rows [m0, m0 + 16*MT), columns [n0, n0 + 16*NT), all of K.  Wave w
-// takes K super-steps s = w, w + WK, ... of 256 bytes; in a super-step lane
-// (r = lane % 16, g = lane / 16) loads 64 contiguous bytes of its B column
-// and of its A row at k = 256*s + 64*g .. +63 and issues four
-// v_mfma_i32_16x16x64_i8, the q-th taking bytes 16q..16q+15 of every lane.
-// The K assignment is a permutation of K that A and B share, so each
-// instruction pairs A(m, k) with B(k, n) for the same k.
+// Block: rows [m0, m0 + 16*MT), columns [n0, n0 + 16*NT), all of K.  K is
+// cut into 256-byte super-steps; wave w takes the batches of SS consecutive
+// super-steps starting at w*SS, w*SS + WK*SS, ...  A batch is loaded in one
+// go (all of its B and A bytes requested before any is used, so a wave keeps
+// SS*(NT+MT) KiB in flight and the whole B stream is requested almost at
+// once), then consumed by four v_mfma_i32_16x16x64_i8 per super-step and
+// instruction tile: instruction q of super-step s covers k = 256 s + 64 q
+// .. +63, lane (r = lane % 16, g = lane / 16) holding k = 256 s + 64 q + 16 g
+// .. +15 of its B column and of its A row (each load instruction reads 64
+// contiguous bytes from each of 16 rows).
 //
 // gemm_skinny_kernel takes column-major B (K-contiguous columns).  FAST:
 // M % (16 MT) == 0, N % (16 NT) == 0, K % 256 == 0, 16-byte aligned A, B, C,
@@ -32,10 +35,11 @@
 #pragma once
 
 #include "device_common.h"
+#include "rc_pipelined_kernel.h"  // LDS-DMA helpers
 
 namespace tdi8 {
 
-template <int MT, int NT, int WK, bool FAST>
+template <int MT, int NT, int WK, int SS, bool FAST>
 __global__ void __launch_bounds__(WK * 64) gemm_skinny_kernel(GemmArgs g) {
     constexpr int BM = 16 * MT;
     constexpr int BN = 16 * NT;
@@ -51,6 +55,22 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_kernel(GemmArgs g) {
     const int m0 = blockIdx.y * BM;
     const int n0 = blockIdx.x * BN;
 
+    const int8_t *bp[NT];
+    const int8_t *ap[MT];
+    int bcol_ok[NT], arow_ok[MT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int col = n0 + 16 * j + r16;
+        bcol_ok[j] = FAST || col < g.N;
+        bp[j] = g.B + static_cast<int64_t>(bcol_ok[j] ? col : 0) * g.ldb + 16 * grp;
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int row = m0 + 16 * i + r16;
+        arow_ok[i] = FAST || row < g.M;
+        ap[i] = g.A + static_cast<int64_t>(arow_ok[i] ? row : 0) * g.lda + 16 * grp;
+    }
+
     i32x4 acc[MT][NT];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -58,34 +78,43 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_kernel(GemmArgs g) {
         for (int j = 0; j < NT; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
     const int nss = (g.K + 255) / 256;
-    for (int s = wave; s < nss; s += WK) {
-        const int kb = 256 * s + 64 * grp;
-        i32x4 xb[NT][4], xa[MT][4];
+    for (int s0 = wave * SS; s0 < nss; s0 += WK * SS) {
+        i32x4 xb[SS][NT][4], xa[SS][MT][4];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int col = n0 + 16 * j + r16;
-            const int8_t *p = g.B + static_cast<int64_t>(col) * g.ldb + kb;
+        for (int u = 0; u < SS; ++u) {
+            const int s = s0 + u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k = 256 * s + 64 * q + 16 * grp;  // this lane's first K
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int8_t *p = bp[j] + 256 * s + 64 * q;
+                    if (FAST)
+                        xb[u][j][q] = s < nss ? load16(p) : i32x4{0, 0, 0, 0};
+                    else
+                        xb[u][j][q] = load16_masked(p, (bcol_ok[j] && s < nss) ? clamp16(g.K - k) : 0);
+                }
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    const int8_t *p = ap[i] + 256 * s + 64 * q;
+                    if (FAST)
+                        xa[u][i][q] = s < nss ? load16(p) : i32x4{0, 0, 0, 0};
+                    else
+                        xa[u][i][q] = load16_masked(p, (arow_ok[i] && s < nss) ? clamp16(g.K - k) : 0);
+                }
+            }
+        }
+        // every load of the batch is in flight before the first use
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < SS; ++u)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                xb[j][q] = FAST ? load16(p + 16 * q)
-                                : load16_masked(p + 16 * q, col < g.N ? clamp16(g.K - (kb + 16 * q)) : 0);
-        }
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            const int row = m0 + 16 * i + r16;
-            const int8_t *p = g.A + static_cast<int64_t>(row) * g.lda + kb;
+                for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                xa[i][q] = FAST ? load16(p + 16 * q)
-                                : load16_masked(p + 16 * q, row < g.M ? clamp16(g.K - (kb + 16 * q)) : 0);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-#pragma unroll
-                for (int j = 0; j < NT; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j][q], xa[i][q], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < NT; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[u][j][q], xa[u][i][q], acc[i][j], 0, 0, 0);
     }
 
 #pragma unroll
@@ -108,7 +137,117 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_kernel(GemmArgs g) {
     }
 }
 
-template <int MT, int WK, bool FAST>
+// Unpredicated skinny kernel for column-major B (used when K % KC == 0 and
+// everything is aligned).  The direct operand loads above read 16 rows x
+// 64 bytes per instruction, which streams poorly from HBM; here every load
+// instruction moves one whole kilobyte of one row of A or B straight into
+// LDS (global_load_lds_dwordx4), so the stream is fully contiguous.  K is
+// taken in chunks of KC bytes, two chunks in flight; a chunk's rows sit in
+// LDS with a 16-byte pad (row stride KC + 16), so the 16 lanes that read
+// one K position of 16 rows hit 16 different bank groups.  After a chunk
+// lands, wave w consumes K positions w*KC/WK .. (w+1)*KC/WK - 1 of it with
+// v_mfma_i32_16x16x64_i8 fed by ds_read_b128, and the WK partial sums are
+// reduced in LDS at the end.
+template <int MT, int NT, int WK, int KC>
+__global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
+    constexpr int BM = 16 * MT;
+    constexpr int BN = 16 * NT;
+    constexpr int TILES = MT * NT;
+    constexpr int ROWS = BM + BN;
+    constexpr int RS = KC + 16;                     // LDS row stride
+    constexpr int PIECES = KC / 1024;               // 1 KiB pieces per row and chunk
+    constexpr int LOADS = ROWS * PIECES;            // wave instructions per chunk
+    constexpr int LPW = LOADS / WK;
+    constexpr int KW = KC / WK;                     // K positions per wave and chunk
+    static_assert(KC % 1024 == 0 && LOADS % WK == 0 && KW % 64 == 0, "chunk must split evenly");
+    static_assert(2 * ROWS * RS <= 160 * 1024 - WK * TILES * 1024, "LDS budget");
+
+#if defined(__HIP_DEVICE_COMPILE__)
+    __shared__ __attribute__((aligned(1024))) int8_t buf[2][ROWS * RS];
+    __shared__ i32x4 red[WK][TILES][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r16 = lane & 15;
+    const int grp = lane >> 4;
+    const int m0 = blockIdx.y * BM;
+    const int n0 = blockIdx.x * BN;
+    const int nch = g.K / KC;
+
+    const int8_t *src[LPW];
+    int dst_off[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int x = i * WK + wave;
+        const int row = x / PIECES;
+        const int piece = x % PIECES;
+        src[i] = (row < BM ? g.A + static_cast<int64_t>(m0 + row) * g.lda
+                           : g.B + static_cast<int64_t>(n0 + row - BM) * g.ldb) + piece * 1024 + 16 * lane;
+        dst_off[i] = row * RS + piece * 1024;
+    }
+    auto issue = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i)
+            __builtin_amdgcn_global_load_lds(src[i] + c * KC, (lds_void_t *)(buf[c & 1] + dst_off[i]), 16, 0, 0);
+    };
+
+    i32x4 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+    if (nch > 0) issue(0);
+    if (nch > 1) issue(1);
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) {
+            TDI8_WAIT_VMCNT(LPW);
+        } else {
+            TDI8_WAIT_VMCNT(0);
+        }
+        __builtin_amdgcn_s_barrier();
+        const int8_t *b = buf[c & 1];
+#pragma unroll
+        for (int kk = 0; kk < KW; kk += 64) {
+            const int k = wave * KW + kk + 16 * grp;
+            i32x4 xa[MT], xb[NT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i) xa[i] = *reinterpret_cast<const i32x4 *>(b + (16 * i + r16) * RS + k);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) xb[j] = *reinterpret_cast<const i32x4 *>(b + (BM + 16 * j + r16) * RS + k);
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j], xa[i], acc[i][j], 0, 0, 0);
+        }
+        if (c + 2 < nch) {
+            TDI8_WAIT_LGKM0();
+            __builtin_amdgcn_s_barrier();  // every wave is done with this buffer
+            issue(c + 2);
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) red[wave][i * NT + j][lane] = acc[i][j];
+    __syncthreads();
+    for (int t = tid; t < TILES * 64; t += WK * 64) {
+        const int tile = t >> 6;
+        const int l = t & 63;
+        i32x4 sum = red[0][tile][l];
+#pragma unroll
+        for (int w = 1; w < WK; ++w) sum += red[w][tile][l];
+        const int m = m0 + 16 * (tile / NT) + (l & 15);
+        const int n = n0 + 16 * (tile % NT) + 4 * (l >> 4);
+        store4<true>(g, m, n, sum);
+    }
+#endif
+}
+
+template <int MT, int WK, int SS, bool FAST>
 __global__ void __launch_bounds__(WK * 64) gemm_skinny_rr_kernel(GemmArgs g) {
     constexpr int BM = 16 * MT;
     constexpr int BN = 64;
@@ -131,32 +270,48 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rr_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
+    // Batches of SS steps of 64 K: wave w takes steps w*SS .. w*SS+SS-1,
+    // then (w + WK)*SS ..; all loads of a batch are issued before use.
     const int nss = (g.K + 63) / 64;
-    for (int s = wave; s < nss; s += WK) {
-        const int kb = 64 * s + 16 * grp;
-        uint32_t w[16];
+    for (int s0 = wave * SS; s0 < nss; s0 += WK * SS) {
+        uint32_t w[SS][16];
+        i32x4 xa[SS][MT];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const int k = kb + t;
-            const int8_t *p = g.B + static_cast<int64_t>(k) * g.ldb + col;
-            w[t] = FAST ? *reinterpret_cast<const uint32_t *>(p) : load4_masked(p, k < g.K ? ncol : 0);
+        for (int u = 0; u < SS; ++u) {
+            const int kb = 64 * (s0 + u) + 16 * grp;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int k = kb + t;
+                const int8_t *p = g.B + static_cast<int64_t>(k < g.K ? k : 0) * g.ldb + col;
+                if (FAST)
+                    w[u][t] = k < g.K ? *reinterpret_cast<const uint32_t *>(p) : 0u;
+                else
+                    w[u][t] = load4_masked(p, k < g.K ? ncol : 0);
+            }
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const int row = m0 + 16 * i + r16;
+                const int8_t *p = g.A + static_cast<int64_t>(row < g.M ? row : 0) * g.lda + (kb < g.K ? kb : 0);
+                xa[u][i] = FAST ? (kb < g.K ? load16(p) : i32x4{0, 0, 0, 0})
+                                : load16_masked(p, row < g.M ? clamp16(g.K - kb) : 0);
+            }
         }
-        i32x4 xb[4];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-            uint32_t t4[4];
-            transpose4x4(&w[4 * qd], t4);
+        for (int u = 0; u < SS; ++u) {
+            i32x4 xb[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xb[j][qd] = static_cast<int32_t>(t4[j]);
-        }
+            for (int qd = 0; qd < 4; ++qd) {
+                uint32_t t4[4];
+                transpose4x4(&w[u][4 * qd], t4);
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            const int row = m0 + 16 * i + r16;
-            const int8_t *p = g.A + static_cast<int64_t>(row) * g.lda + kb;
-            const i32x4 xa = FAST ? load16(p) : load16_masked(p, row < g.M ? clamp16(g.K - kb) : 0);
+                for (int j = 0; j < 4; ++j) xb[j][qd] = static_cast<int32_t>(t4[j]);
+            }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j], xa, acc[i][j], 0, 0, 0);
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j], xa[u][i], acc[i][j], 0, 0, 0);
         }
     }
 
