@@ -33,14 +33,24 @@ __device__ __forceinline__ uint32_t keep_bytes(uint32_t w, int nvalid) {
     return nvalid >= 4 ? w : (nvalid <= 0 ? 0u : (w & ((1u << (8 * nvalid)) - 1u)));
 }
 
-// The first `nvalid` (0..16) bytes at p, any alignment, zero beyond.
-// Only dwords holding at least one wanted byte are read; an aligned dword
-// never straddles a page, so nothing outside the operand's pages is touched.
+// 16 bytes at p, any alignment: one global_load_dwordx4 (the ROCm driver
+// runs gfx9-class GPUs in unaligned-access mode, and the compiler lowers an
+// unaligned 16-byte copy to exactly this instruction).
+__device__ __forceinline__ i32x4 load16_unaligned(const int8_t *p) {
+    i32x4 v;
+    __builtin_memcpy(&v, p, 16);
+    return v;
+}
+
+// The first `nvalid` (0..16) bytes at p, any alignment, zero beyond.  A full
+// chunk is one load; for a partial chunk only dwords holding at least one
+// wanted byte are read (an aligned dword never straddles a page, so nothing
+// outside the operand's pages is touched).
 __device__ __forceinline__ i32x4 load16_masked(const int8_t *p, int nvalid) {
     i32x4 r = {0, 0, 0, 0};
     if (nvalid <= 0) return r;
     const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-    if (nvalid >= 16 && (a & 15) == 0) return load16(p);
+    if (nvalid >= 16) return load16_unaligned(p);
     const uint32_t s = static_cast<uint32_t>(a & 3);
     const uint32_t *w = reinterpret_cast<const uint32_t *>(a - s);
     uint32_t d[5];
@@ -56,7 +66,11 @@ __device__ __forceinline__ i32x4 load16_masked(const int8_t *p, int nvalid) {
 __device__ __forceinline__ uint32_t load4_masked(const int8_t *p, int nvalid) {
     if (nvalid <= 0) return 0u;
     const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-    if (nvalid >= 4 && (a & 3) == 0) return *reinterpret_cast<const uint32_t *>(p);
+    if (nvalid >= 4) {
+        uint32_t v;
+        __builtin_memcpy(&v, p, 4);
+        return v;
+    }
     const uint32_t s = static_cast<uint32_t>(a & 3);
     const uint32_t *w = reinterpret_cast<const uint32_t *>(a - s);
     const uint32_t d0 = w[0];
@@ -83,8 +97,8 @@ __device__ __forceinline__ void store4(const GemmArgs &g, int m, int n, i32x4 v)
     }
     if (m >= g.M) return;
     int32_t *p = g.C + static_cast<int64_t>(m) * g.ldc + n;
-    if (n + 3 < g.N && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
-        *reinterpret_cast<i32x4 *>(p) = v;
+    if (n + 3 < g.N) {
+        __builtin_memcpy(p, &v, 16);  // one global_store_dwordx4, 4-byte aligned
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
