@@ -27,13 +27,13 @@
 #pragma once
 
 #define TDI8_CONFIG_LIST(X)                                          \
-    X(0, 0, 32, 2, 2, 1, 4, 4, 64, 4)   /* 256 x 256, 4 waves */     \
+    X(0, 0, 32, 2, 4, 1, 4, 2, 128, 2)  /* 256 x 256, 8 waves */     \
     X(1, 0, 32, 2, 2, 1, 2, 4, 64, 4)   /* 128 x 256, 4 waves */     \
     X(2, 0, 32, 2, 2, 1, 4, 2, 64, 4)   /* 256 x 128, 4 waves */     \
     X(3, 0, 32, 2, 2, 1, 2, 2, 64, 4)   /* 128 x 128, 4 waves */     \
     X(4, 0, 32, 2, 2, 1, 2, 1, 64, 4)   /* 128 x  64, 4 waves */     \
     X(5, 0, 32, 2, 2, 1, 1, 1, 64, 4)   /*  64 x  64, reuse 1 */     \
-    X(6, 0, 32, 2, 4, 1, 4, 2, 128, 2)  /* 256 x 256, 8 waves */     \
+    X(6, 0, 32, 2, 2, 1, 4, 4, 64, 4)   /* 256 x 256, 4 waves */     \
     X(7, 0, 32, 2, 4, 1, 1, 1, 128, 2)  /*  64 x 128, reuse 1 */     \
     X(8, 0, 32, 4, 2, 1, 2, 4, 128, 2)  /* 256 x 256, 8 waves */     \
     X(9, 0, 32, 4, 2, 1, 1, 1, 128, 2)  /* 128 x  64, reuse 1 */     \

@@ -18,9 +18,9 @@ namespace tdi8 {
 
 template <class P, bool BCOL, bool FAST>
 static const void *entry() {
-    if constexpr (P::family == 0 && BCOL && FAST)
+    if constexpr (P::family == 0 && FAST)
         return reinterpret_cast<const void *>(
-            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, P::st>);
+            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, P::st, !BCOL>);
     else if constexpr (P::family == 0)
         return reinterpret_cast<const void *>(
             &gemm_tiled_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, BCOL, FAST>);

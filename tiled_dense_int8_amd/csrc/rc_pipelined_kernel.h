@@ -52,7 +52,17 @@ __device__ __forceinline__ void tile_of_block(const GemmArgs &g, int bid, int &t
     tn = within / rows;
 }
 
-template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES>
+// Permutation of the 16-byte chunks of a row-major B row k in LDS (BN bytes
+// per row): even values only, varying with k so that the eight rows read by
+// one 16-lane group of a transpose read land on distinct bank groups.
+template <int BN>
+__device__ __forceinline__ int brow_swizzle(int k) {
+    constexpr int CPRB = BN / 16;
+    constexpr int P = BN >= 256 ? 1 : 256 / BN;  // rows sharing one 256-byte bank window
+    return 2 * ((k / P) % (CPRB / 2));
+}
+
+template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArgs g) {
     constexpr int NW = WM * WN;
     constexpr int BM = WM * MF * MT;
@@ -60,6 +70,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
     constexpr int CPR = BK / 16;
     constexpr int A_CHUNKS = BM * CPR;
     constexpr int STAGE = (BM + BN) * BK;
+    constexpr int A_BYTES_ = BM * BK;
     constexpr int LOADS = STAGE / 1024;          // 1 KiB wave instructions per stage
     constexpr int LPW = LOADS / NW;              // per wave
     constexpr int KSTEP = Mfma<MF>::KSTEP;
@@ -69,6 +80,8 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
     static_assert(A_CHUNKS % 64 == 0, "A region must be whole wave instructions");
     static_assert(STAGES >= 2, "at least two stages");
     static_assert(KS % 2 == 0, "operand double buffer needs an even number of K steps per tile");
+    constexpr int CPRB = BN / 16;                // 16-byte chunks per row-major B row
+    static_assert(!BROW || (MF == 32 && CPRB >= 4 && (BK * BN) % 1024 == 0), "row-major B form");
     using Acc = typename Mfma<MF>::Acc;
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
 
@@ -93,16 +106,27 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
             const int r = q / CPR;
             const int c = (q % CPR) ^ chunk_swizzle<CPR>(r);
             src[i] = g.A + static_cast<int64_t>(m0 + r) * g.lda + 16 * c;
-        } else {
+        } else if constexpr (!BROW) {
             const int qb = q - A_CHUNKS;
             const int r = qb / CPR;
             const int c = (qb % CPR) ^ chunk_swizzle<CPR>(r);
             src[i] = g.B + static_cast<int64_t>(n0 + r) * g.ldb + 16 * c;
+        } else {
+            // row-major B: LDS row k of the tile holds B(k0 + k, n0 .. n0+BN-1)
+            const int qb = q - A_CHUNKS;
+            const int k = qb / CPRB;
+            const int c = (qb % CPRB) ^ brow_swizzle<BN>(k);
+            src[i] = g.B + static_cast<int64_t>(k) * g.ldb + n0 + 16 * c;
         }
     }
+    // K offset of tile kt for load instruction i.
+    auto koff = [&](int i, int kt) -> int64_t {
+        const bool is_b = (i * NW + wave) * 64 >= A_CHUNKS;
+        return (BROW && is_b) ? static_cast<int64_t>(kt) * BK * g.ldb : static_cast<int64_t>(kt) * BK;
+    };
     auto issue_one = [&](int kt, int i) {
         int8_t *dst = lds + (kt % STAGES) * STAGE + (i * NW + wave) * 1024;
-        __builtin_amdgcn_global_load_lds(src[i] + kt * BK, (lds_void_t *)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src[i] + koff(i, kt), (lds_void_t *)dst, 16, 0, 0);
     };
     auto issue = [&](int kt) {
 #pragma unroll
@@ -126,6 +150,26 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
         swb[j] = chunk_swizzle<CPR>(r - BM);
     }
 
+    // Row-major B operands come from two transpose reads per fragment.  In
+    // each 16-lane group, lanes 2r and 2r+1 address the two 8-byte halves of
+    // row r of an 8 x 16-byte block and lane c receives column c (eight K
+    // values).  For the 32x32x32 operand, lane l (group q = l / 16, c = l % 16)
+    // needs column n = l % 32 and K = 16 (l / 32) .. +15: group q reads
+    // columns 16 (q % 2) .. +15 of K rows 16 (q / 2) + (0..7) and then + 8.
+    int offbt[NT][2];
+    if constexpr (BROW) {
+        const int q = lane >> 4, c = lane & 15;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int nb = wn * (NT * MF) + j * MF + 16 * (q & 1);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int k = 16 * (q >> 1) + 8 * half + (c >> 1);
+                offbt[j][half] = A_BYTES_ + k * BN + 16 * ((nb >> 4) ^ brow_swizzle<BN>(k)) + 8 * (c & 1);
+            }
+        }
+    }
+
     Acc acc[MT][NT];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -136,20 +180,24 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
     auto read_one = [&](int kt, int ks, int buf, int r) {
         const int8_t *base = lds + (kt % STAGES) * STAGE;
         const int c = ks * KC + lgrp;
-        if (r < MT)
+        if (r < MT) {
             fa[buf][r] = *reinterpret_cast<const i32x4 *>(base + offa[r] + 16 * (c ^ swa[r]));
-        else
+        } else if constexpr (!BROW) {
             fb[buf][r - MT] = *reinterpret_cast<const i32x4 *>(base + offb[r - MT] + 16 * (c ^ swb[r - MT]));
+        } else {
+            // K step ks is 32 rows further down; the swizzle repeats every 32 rows
+            const int8_t *p0 = base + offbt[r - MT][0] + ks * MF * BN;
+            const int8_t *p1 = base + offbt[r - MT][1] + ks * MF * BN;
+            typedef int v2i_t __attribute__((ext_vector_type(2)));
+            typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
+            const v2i_t lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)(p0));
+            const v2i_t hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)(p1));
+            fb[buf][r - MT] = i32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
     };
     auto read_frags = [&](int kt, int ks, int buf) {
-        const int8_t *base = lds + (kt % STAGES) * STAGE;
-        const int c = ks * KC + lgrp;
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
-            fa[buf][i] = *reinterpret_cast<const i32x4 *>(base + offa[i] + 16 * (c ^ swa[i]));
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-            fb[buf][j] = *reinterpret_cast<const i32x4 *>(base + offb[j] + 16 * (c ^ swb[j]));
+        for (int r = 0; r < MT + NT; ++r) read_one(kt, ks, buf, r);
     };
     constexpr int F = MT * NT;   // matrix-core instructions per K step
     constexpr int R = MT + NT;   // operand reads per K step
