@@ -226,3 +226,31 @@ def test_workload_large_16384(lib, bcm):
     lib.gemm(A_dev, B_dev, bcm, out=C_dev)
     torch.cuda.synchronize()
     sampled_check(C_dev, A, Bs, bcm, M, N, K, seed=0, n_random=8192, freivalds=2)
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_int32_limit_and_wrap(lib, bcm):
+    """All -128 operands at the largest K without overflow, and one step past
+    it: the result is defined mod 2^32 (what int32 accumulation gives), so
+    16384 * 131073 must wrap to its two's-complement value, not saturate."""
+    t = lib
+    for K in (131071, 131073):
+        exact = 16384 * K
+        want = ((exact + 2 ** 31) % 2 ** 32) - 2 ** 31
+        for (M, N) in [(16, 64), (64, 128)]:
+            A = np.full((M, K), -128, np.int8)
+            B = np.full((K, N), -128, np.int8)
+            C = check_case(DeviceCase(A, B, bcm), f"K={K} all -128", expect=np.full((M, N), want, np.int32))
+            assert int(C[0, 0]) == want
+        # and through a general-family configuration
+        A = np.full((64, K), -128, np.int8)
+        B = np.full((K, 128), -128, np.int8)
+        check_case(DeviceCase(A, B, bcm), f"K={K} cfg7", config=7, expect=np.full((64, 128), want, np.int32))
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_long_k_random(lib, bcm):
+    """Random operands over a long K (many K tiles and skinny chunks)."""
+    for (M, N, K) in [(16, 256, 65536), (256, 256, 32768), (33, 70, 20000)]:
+        A, B = synthetic.gemm_inputs(M, N, K, seed=5)
+        check_case(DeviceCase(A, B, bcm), f"long K {M}x{N}x{K}")
