@@ -136,7 +136,8 @@ int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, cons
         g.tiles_m = static_cast<int>(tm);
         g.tiles_n = static_cast<int>(tn);
         grid = dim3(static_cast<unsigned>(tm * tn));
-        const bool b_ok = bcol ? (aligned(B, 16) && ldb % 16 == 0) : (aligned(B, 4) && ldb % 4 == 0);
+        // both B layouts are moved by 16-byte LDS DMA loads in the fast form
+        const bool b_ok = aligned(B, 16) && ldb % 16 == 0;
         fast = M % c.bm == 0 && N % c.bn == 0 && K % c.bk == 0 && a_ok && b_ok && c_ok;
     } else {
         const int bn = bcol ? c.bn : 64;

@@ -1,8 +1,10 @@
-// Unpredicated int8 GEMM kernel for column-major B on gfx950: the form the
-// dispatcher uses when every dimension is a tile multiple and the operands
-// are 16-byte aligned (A row-major and B column-major are then both
-// K-contiguous, so both tiles can go from HBM to LDS with no register
-// staging).
+// Unpredicated int8 GEMM kernel on gfx950: the form the dispatcher uses when
+// every dimension is a tile multiple and the operands are 16-byte aligned.
+// A (row-major) and column-major B are K-contiguous, so their tiles go from
+// HBM to LDS as K-contiguous rows.  Row-major B (BROW) is copied as it lies,
+// BK rows of BN contiguous bytes, and its operand fragments are gathered
+// K-major out of LDS with the transpose read ds_read_b64_tr_b8, so neither
+// layout is staged or transposed in registers.
 //
 // Differences from gemm_tiled_kernel:
 //  * global -> LDS with global_load_lds_dwordx4: each wave instruction moves
