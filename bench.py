@@ -154,8 +154,8 @@ def check_sample(w, A, Bs, C_dev, n=256):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="square4096", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-skinny", action="store_true")
@@ -226,7 +226,7 @@ def main():
 
     if not args.no_skinny and args.workload == "square4096":
         ws = WORKLOADS["skinny16"]
-        s_wall, s_kern, s_cfg, s_sets, sA, sB, ssets = time_workload(t, ws, max(args.steps, 200), args.warmup)
+        s_wall, s_kern, s_cfg, s_sets, sA, sB, ssets = time_workload(t, ws, max(args.steps, 1000), max(args.warmup, 1000))
         s_ok = check_sample(ws, sA, sB, ssets[0][2])
         byts = ws["M"] * ws["K"] + ws["K"] * ws["N"] + 4 * ws["M"] * ws["N"]
         gbs = byts / (s_kern * 1e-3) / 1e9

@@ -10,10 +10,10 @@
 //  * global -> LDS with global_load_lds_dwordx4: each wave instruction moves
 //    1 KiB straight into LDS (lane l's 16 bytes land at l*16 of the block),
 //    so no VGPRs hold staged tiles and no ds_write is issued;
-//  * STAGES LDS buffers; loads run STAGES-1 K tiles ahead, and one barrier
-//    per K tile both publishes the next tile and retires the oldest buffer
-//    (prefetch = double buffering generalised; "CUDA编程实践" section 3, the
-//    data-prefetch paragraph);
+//  * STAGES LDS buffers; one barrier per K tile both publishes the next
+//    tile and frees the buffer just consumed, which is refilled at once with
+//    the tile STAGES ahead (prefetch = double buffering generalised;
+//    "CUDA编程实践" section 3, the data-prefetch paragraph);
 //  * instruction operands are prefetched one K step ahead in registers; the
 //    first step of the next K tile is read right after the barrier, under
 //    the last step's matrix-core work;
@@ -207,23 +207,33 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
         const int i = x / NT, j = x % NT;
         acc[i][j] = Mfma<MF>::run(fb[buf][j], fa[buf][i], acc[i][j]);
     };
-    constexpr int NS = (KS - 1) * F;  // matrix-core slots before the last K step
+    // Read r of a K step is issued after matrix instruction r / 2: two per
+    // instruction, at the front of the step, so the last one has most of the
+    // step to land before the step's closing wait.
+    auto read_slot = [](int r) constexpr -> int { return r / 2 < F ? r / 2 : F - 1; };
 
     // One K tile, as a fixed instruction order (each matrix-core instruction
     // followed by the memory operations slotted after it, fenced so the
     // compiler keeps the order):
-    //  * K steps 0 .. KS-2: after matrix instruction x of step ks, the read
-    //    of operand x of step ks+1 (reads front-loaded, so they land before
-    //    the step ends), and the DMA loads of the refill of the oldest
-    //    buffer spread evenly over these (KS-1)*F slots (LOAD);
-    //  * last step: half of its matrix work, then publish tile t+1 (own DMA
-    //    loads and operand reads done, then a barrier), then the other half
-    //    with tile t+1's first-step operands read after each instruction.
-    // Each step ends by retiring its operand reads, so the next step's
-    // matrix work starts with its operands in registers.
-    auto tile = [&](int t, auto load_tag, auto next_tag) {
+    //  * K steps 0 .. KS-2: matrix work of the step, with the operand reads
+    //    of the next step slotted in (read_slot);
+    //  * last step: its operands are already in registers, so first publish
+    //    tile t+1 (own DMA loads of t+1 retired, then a barrier: every wave
+    //    is done with buffer t % STAGES), refill that buffer with tile
+    //    t+STAGES at once, then the step's matrix work with tile t+1's
+    //    first-step operands read in between.
+    // Every step ends by retiring its operand reads, so the next step's
+    // matrix work starts with its operands in registers.  Issuing a refill
+    // right after the barrier that frees its buffer gives it the longest
+    // possible time in flight (a whole K tile with two stages).
+    //   LOAD:  issue tile t+STAGES after the barrier;
+    //   NEXT:  tile t+1 exists (barrier, next-tile reads);
+    //   WAITN: the loads of tiles t+2 .. t+STAGES-1 are in flight and may
+    //          stay so; otherwise wait for every outstanding load.
+    auto tile = [&](int t, auto load_tag, auto next_tag, auto waitn_tag) {
         constexpr bool LOAD = decltype(load_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
+        constexpr bool WAITN = decltype(waitn_tag)::value;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int cur = ks & 1;
@@ -231,29 +241,14 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
 #pragma unroll
                 for (int x = 0; x < F; ++x) {
                     mma_one(cur, x);
-                    if (x < R) read_one(t, ks + 1, cur ^ 1, x);
-                    if (x == F - 1)
 #pragma unroll
-                        for (int r = F; r < R; ++r) read_one(t, ks + 1, cur ^ 1, r);
-                    if constexpr (LOAD) {
-                        const int gx = ks * F + x;
-#pragma unroll
-                        for (int li = 0; li < LPW; ++li)
-                            if ((li * NS) / LPW == gx) issue_one(t + STAGES - 1, li);
-                    }
+                    for (int r = 0; r < R; ++r)
+                        if (read_slot(r) == x) read_one(t, ks + 1, cur ^ 1, r);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
-                constexpr int H = F / 2;
-#pragma unroll
-                for (int x = 0; x < H; ++x) {
-                    mma_one(cur, x);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
                 if constexpr (NEXT) {
-                    // Loads issued after tile t+1's: the refills of tiles
-                    // t+2 .. t+STAGES-1.
-                    if constexpr (LOAD) {
+                    if constexpr (WAITN) {
                         TDI8_WAIT_VMCNT((STAGES - 2) * LPW);
                     } else {
                         TDI8_WAIT_VMCNT(0);
@@ -262,14 +257,17 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
                     __builtin_amdgcn_s_barrier();
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                if constexpr (LOAD) {
+                    issue(t + STAGES);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
 #pragma unroll
-                for (int x = H; x < F; ++x) {
+                for (int x = 0; x < F; ++x) {
                     mma_one(cur, x);
                     if constexpr (NEXT) {
-                        if (x - H < R) read_one(t + 1, 0, cur ^ 1, x - H);
-                        if (x == F - 1)
 #pragma unroll
-                            for (int r = F - H; r < R; ++r) read_one(t + 1, 0, cur ^ 1, r);
+                        for (int r = 0; r < R; ++r)
+                            if (read_slot(r) == x) read_one(t + 1, 0, cur ^ 1, r);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -278,13 +276,15 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    using T1 = std::true_type;
+    using T0 = std::false_type;
 
     if (nk > 0) {
-        // Prologue: tiles 0 .. STAGES-2 in flight, wait for tile 0.
-        if (nk >= STAGES - 1) {
+        // Prologue: every buffer filled (tiles 0 .. STAGES-1), wait for tile 0.
+        if (nk >= STAGES) {
 #pragma unroll
-            for (int s = 0; s < STAGES - 1; ++s) issue(s);
-            TDI8_WAIT_VMCNT((STAGES - 2) * LPW);
+            for (int s = 0; s < STAGES; ++s) issue(s);
+            TDI8_WAIT_VMCNT((STAGES - 1) * LPW);
         } else {
             for (int s = 0; s < nk; ++s) issue(s);
             TDI8_WAIT_VMCNT(0);
@@ -294,12 +294,17 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
         TDI8_WAIT_LGKM0();  // the K loop starts with no operand read pending
         __builtin_amdgcn_sched_barrier(0);
 
-        // Steady state: every iteration refills a buffer and has a successor.
         int t = 0;
-        for (; t + STAGES - 1 < nk; ++t) tile(t, std::true_type{}, std::true_type{});
-        // Drain: nothing left to fetch.
-        for (; t + 1 < nk; ++t) tile(t, std::false_type{}, std::true_type{});
-        tile(t, std::false_type{}, std::false_type{});
+        // Steady state: every iteration refills the buffer it frees.
+        for (; t + STAGES < nk; ++t) tile(t, T1{}, T1{}, T1{});
+        // Last refill was issued one iteration ago: tiles t+2 .. nk-1 in flight.
+        if (t + STAGES == nk && t + 1 < nk) {
+            tile(t, T0{}, T1{}, T1{});
+            ++t;
+        }
+        // Drain: wait for everything outstanding.
+        for (; t + 1 < nk; ++t) tile(t, T0{}, T1{}, T0{});
+        tile(t, T0{}, T0{}, T0{});
     }
 
     // Epilogue: lane holds C[m][n .. n+3] per group of four accumulators.
