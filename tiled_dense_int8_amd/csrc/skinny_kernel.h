@@ -160,11 +160,11 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
     constexpr int LPW = LOADS / WK;
     constexpr int KW = KC / WK;                     // K positions per wave and chunk
     static_assert(KC % 1024 == 0 && LOADS % WK == 0 && KW % 64 == 0, "chunk must split evenly");
-    static_assert(2 * ROWS * RS <= 160 * 1024 - WK * TILES * 1024, "LDS budget");
+    static_assert(2 * ROWS * RS <= 160 * 1024 - TILES * 1024, "LDS budget");
 
 #if defined(__HIP_DEVICE_COMPILE__)
     __shared__ __attribute__((aligned(1024))) int8_t buf[2][ROWS * RS];
-    __shared__ i32x4 red[WK][TILES][64];
+    __shared__ int32_t red[TILES][64][4];   // block sum, accumulated with LDS atomics
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -198,6 +198,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
+    for (int t = tid; t < TILES * 64 * 4; t += WK * 64) (&red[0][0][0])[t] = 0;
     if (nch > 0) issue(0);
     if (nch > 1) issue(1);
     for (int c = 0; c < nch; ++c) {
@@ -229,17 +230,20 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
         }
     }
 
+    // Sum the waves' partial tiles: integer addition is exact in any order,
+    // so every wave adds its tile into one LDS copy with atomics.
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NT; ++j) red[wave][i * NT + j][lane] = acc[i][j];
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) atomicAdd(&red[i * NT + j][lane][e], acc[i][j][e]);
     __syncthreads();
     for (int t = tid; t < TILES * 64; t += WK * 64) {
         const int tile = t >> 6;
         const int l = t & 63;
-        i32x4 sum = red[0][tile][l];
-#pragma unroll
-        for (int w = 1; w < WK; ++w) sum += red[w][tile][l];
+        const i32x4 sum = {red[tile][l][0], red[tile][l][1], red[tile][l][2], red[tile][l][3]};
         const int m = m0 + 16 * (tile / NT) + (l & 15);
         const int n = n0 + 16 * (tile % NT) + 4 * (l >> 4);
         store4<true>(g, m, n, sum);
