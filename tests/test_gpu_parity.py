@@ -34,7 +34,8 @@ def shapes_for(c):
     out = [(BM, BN, BK), (2 * BM, 2 * BN, 2 * BK), (BM + 1, BN - 1, BK + 27), (1, 1, 1), (17, 33, 63),
            (3, 200, 4), (255, 257, 777), (64, 64, 65)]
     if c.family == 1:
-        out += [(BM, 64, 64), (BM, 128, 256)]
+        # the last two: unpredicated forms with 8 and 24 column blocks (block renumbering across XCDs)
+        out += [(BM, 64, 64), (BM, 128, 256), (BM, 8 * BN, 2 * BK), (2 * BM, 24 * BN, BK)]
     return out
 
 

@@ -140,7 +140,10 @@ int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, cons
         const bool b_ok = aligned(B, 16) && ldb % 16 == 0;
         fast = M % c.bm == 0 && N % c.bn == 0 && K % c.bk == 0 && a_ok && b_ok && c_ok;
     } else {
-        const int bn = bcol ? c.bn : 64;
+        // the unpredicated forms move B by 16-byte LDS DMA loads in both layouts
+        fast = M % c.bm == 0 && N % c.bn == 0 && K % c.bk == 0 && a_ok && aligned(B, 16) && ldb % 16 == 0 && c_ok;
+        // the predicated row-major form covers 64 columns per block
+        const int bn = (bcol || fast) ? c.bn : 64;
         const int64_t tm = (M + static_cast<int64_t>(c.bm) - 1) / c.bm;
         const int64_t tn = (N + static_cast<int64_t>(bn) - 1) / bn;
         if (tm > 65535) return TDI8_ERR_BAD_CONFIG;
@@ -148,10 +151,6 @@ int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, cons
         g.tiles_m = static_cast<int>(tm);
         g.tiles_n = static_cast<int>(tn);
         grid = dim3(static_cast<unsigned>(tn), static_cast<unsigned>(tm));
-        if (bcol)
-            fast = M % c.bm == 0 && N % bn == 0 && K % c.bk == 0 && a_ok && aligned(B, 16) && ldb % 16 == 0 && c_ok;
-        else
-            fast = M % c.bm == 0 && N % bn == 0 && K % 64 == 0 && a_ok && aligned(B, 4) && ldb % 4 == 0 && c_ok;
     }
     const void *k = kernels()[id].kernel[bcol ? 1 : 0][fast ? 1 : 0];
     void *args[] = {&g};

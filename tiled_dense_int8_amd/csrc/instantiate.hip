@@ -28,8 +28,10 @@ static const void *entry() {
         return reinterpret_cast<const void *>(&gemm_skinny_lds_kernel<P::mt, P::nt, P::wk, P::bk>);
     else if constexpr (BCOL)
         return reinterpret_cast<const void *>(&gemm_skinny_kernel<P::mt, P::nt, P::wk, P::st, false>);
+    else if constexpr (FAST)
+        return reinterpret_cast<const void *>(&gemm_skinny_rrlds_kernel<P::mt, P::nt, P::wk, P::bk>);
     else
-        return reinterpret_cast<const void *>(&gemm_skinny_rr_kernel<P::mt, P::wk, 2, FAST>);
+        return reinterpret_cast<const void *>(&gemm_skinny_rr_kernel<P::mt, P::wk, 2, false>);
 }
 
 void TDI8_CAT(register_cfg_, TDI8_CFG)(KernelSet *ks) {

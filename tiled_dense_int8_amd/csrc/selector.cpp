@@ -62,7 +62,7 @@ StaticCfg static_cfg(int id) {
     s.threads = 64 * d.wm * d.wn * d.wk;
     s.mfma_k = d.mf == 32 ? 32 : 64;
     s.lds_bytes = d.family == 0 ? d.st * (s.bm + s.bn) * d.bk
-                                : 2 * (s.bm + s.bn) * (d.bk + 16) + d.wk * d.mt * d.nt * 64 * 16;
+                                : 2 * (s.bm + s.bn) * (d.bk + 16) + d.mt * d.nt * 64 * 16;
     s.reuse1_id = -1;
     for (const Desc &e : kDesc) {
         if (e.family == d.family && e.mf == d.mf && e.wm == d.wm && e.wn == d.wn && e.wk == d.wk &&

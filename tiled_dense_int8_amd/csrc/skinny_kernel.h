@@ -25,13 +25,12 @@
 // M % (16 MT) == 0, N % (16 NT) == 0, K % 256 == 0, 16-byte aligned A, B, C,
 // lda and ldb multiples of 16, ldc of 4.
 //
-// gemm_skinny_rr_kernel takes row-major B (N contiguous).  There lane
-// (r, g) reads, for the 16 rows k = 64*s + 16*g .. +15, the dword holding
-// columns n0 + 4r .. +3, transposes the 16 x 4 bytes in registers, and feeds
-// column n0 + 4r + j to instruction j (j = 0..3); one block therefore covers
-// 64 columns.  FAST: M % (16 MT) == 0, N % 64 == 0, K % 64 == 0, 16-byte
-// aligned A and C, lda multiple of 16, 4-byte aligned B, ldb multiple of 4,
-// ldc of 4.
+// gemm_skinny_rr_kernel takes row-major B (N contiguous) in the predicated
+// form.  There lane (r, g) reads, for the 16 rows k = 64*s + 16*g .. +15,
+// the dword holding columns n0 + 4r .. +3, transposes the 16 x 4 bytes in
+// registers, and feeds column n0 + 4r + j to instruction j (j = 0..3); one
+// block therefore covers 64 columns.  Aligned row-major shapes go to
+// gemm_skinny_rrlds_kernel below.
 #pragma once
 
 #include "device_common.h"
@@ -232,6 +231,155 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
 
     // Sum the waves' partial tiles: integer addition is exact in any order,
     // so every wave adds its tile into one LDS copy with atomics.
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) atomicAdd(&red[i * NT + j][lane][e], acc[i][j][e]);
+    __syncthreads();
+    for (int t = tid; t < TILES * 64; t += WK * 64) {
+        const int tile = t >> 6;
+        const int l = t & 63;
+        const i32x4 sum = {red[tile][l][0], red[tile][l][1], red[tile][l][2], red[tile][l][3]};
+        const int m = m0 + 16 * (tile / NT) + (l & 15);
+        const int n = n0 + 16 * (tile % NT) + 4 * (l >> 4);
+        store4<true>(g, m, n, sum);
+    }
+#endif
+}
+
+// Unpredicated skinny kernel for row-major B (used when N % (16 NT) == 0,
+// K % KC == 0 and everything is 16-byte aligned).  Each block covers 16 NT
+// columns (so that N = 4096 still gives 256 blocks); a column block's B is
+// then 16 bytes of every K row.  One load instruction moves 64 such pieces,
+// one per lane, into a 1 KiB LDS group holding 64 K rows of one 16-column
+// sub-block; A rows move as whole kilobytes as in gemm_skinny_lds_kernel.
+// The K-major B operand of v_mfma_i32_16x16x64_i8 is then gathered with
+// ds_read_b64_tr_b8: within each 16-lane group, lanes 2r and 2r+1 address
+// the two 8-byte halves of row r of an 8 x 16-byte block and lane c
+// receives column c (eight K values).  Lane group q needs K rows
+// 16q .. 16q+15 of the 64-row step, so row k' of a group is stored in slot
+// (k' % 8) + 8 ((k' / 16) % 4) + 32 ((k' / 8) % 2): the eight rows one
+// transpose read of group q touches are then 128 contiguous bytes at 128 q
+// (low half) or 512 + 128 q (high half), and the lanes of one LDS pass hit
+// 64 different banks.  Column blocks are renumbered so that the 8 blocks
+// sharing one 128-byte line of a B row run on the same XCD (blocks are dealt
+// to the 8 XCDs round-robin) and meet in its L2.
+template <int MT, int NT, int WK, int KC>
+__global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) {
+    constexpr int BM = 16 * MT;
+    constexpr int BN = 16 * NT;
+    constexpr int TILES = MT * NT;
+    constexpr int RS = KC + 16;                     // LDS row stride of A
+    constexpr int PIECES = KC / 1024;               // 1 KiB pieces per A row and chunk
+    constexpr int A_LOADS = BM * PIECES;
+    constexpr int GROUPS = KC / 64;                 // 64-row groups per B sub-block and chunk
+    constexpr int LOADS = A_LOADS + NT * GROUPS;    // wave instructions per chunk
+    constexpr int LPW = LOADS / WK;
+    constexpr int KW = KC / WK;                     // K positions per wave and chunk
+    constexpr int A_REGION = BM * RS;
+    constexpr int STAGE = A_REGION + NT * KC * 16;
+    static_assert(KC % 1024 == 0 && LOADS % WK == 0 && KW % 64 == 0, "chunk must split evenly");
+    static_assert(2 * STAGE <= 160 * 1024 - TILES * 1024, "LDS budget");
+
+#if defined(__HIP_DEVICE_COMPILE__)
+    __shared__ __attribute__((aligned(1024))) int8_t buf[2][STAGE];
+    __shared__ int32_t red[TILES][64][4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r16 = lane & 15;
+    const int grp = lane >> 4;
+    const int nb = gridDim.x;
+    const int cb = (nb & 7) == 0 ? (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+    const int m0 = blockIdx.y * BM;
+    const int n0 = cb * BN;
+    const int nch = g.K / KC;
+
+    // K row of this lane's piece within a 64-row group (inverse of the slot map)
+    const int krow = (lane & 7) + 8 * (lane >> 5) + 16 * ((lane >> 3) & 3);
+    const int8_t *src[LPW];
+    int dst_off[LPW];
+    bool is_b[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int x = i * WK + wave;
+        if (x < A_LOADS) {
+            const int row = x / PIECES;
+            const int piece = x % PIECES;
+            src[i] = g.A + static_cast<int64_t>(m0 + row) * g.lda + piece * 1024 + 16 * lane;
+            dst_off[i] = row * RS + piece * 1024;
+            is_b[i] = false;
+        } else {
+            const int xb = x - A_LOADS;
+            const int j = xb / GROUPS;
+            const int grp64 = xb % GROUPS;
+            src[i] = g.B + static_cast<int64_t>(64 * grp64 + krow) * g.ldb + n0 + 16 * j;
+            dst_off[i] = A_REGION + j * KC * 16 + grp64 * 1024;
+            is_b[i] = true;
+        }
+    }
+    auto issue = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int64_t off = is_b[i] ? static_cast<int64_t>(c) * KC * g.ldb : static_cast<int64_t>(c) * KC;
+            __builtin_amdgcn_global_load_lds(src[i] + off, (lds_void_t *)(buf[c & 1] + dst_off[i]), 16, 0, 0);
+        }
+    };
+
+    // transpose-read offsets (within a 64-row group) of this lane: row r16/2, half r16%2
+    const int tr_lo = ((r16 >> 1) + 8 * grp) * 16 + 8 * (r16 & 1);
+    const int tr_hi = tr_lo + 32 * 16;
+
+    i32x4 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+    for (int t = tid; t < TILES * 64 * 4; t += WK * 64) (&red[0][0][0])[t] = 0;
+    if (nch > 0) issue(0);
+    if (nch > 1) issue(1);
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) {
+            TDI8_WAIT_VMCNT(LPW);
+        } else {
+            TDI8_WAIT_VMCNT(0);
+        }
+        __builtin_amdgcn_s_barrier();
+        const int8_t *b = buf[c & 1];
+#pragma unroll
+        for (int kk = 0; kk < KW; kk += 64) {
+            const int kb = wave * KW + kk;
+            i32x4 xa[MT], xb[NT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+                xa[i] = *reinterpret_cast<const i32x4 *>(b + (16 * i + r16) * RS + kb + 16 * grp);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int8_t *base = b + A_REGION + j * KC * 16 + (kb >> 6) * 1024;
+                typedef int v2i_t __attribute__((ext_vector_type(2)));
+                typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
+                const v2i_t lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)(base + tr_lo));
+                const v2i_t hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)(base + tr_hi));
+                xb[j] = i32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j], xa[i], acc[i][j], 0, 0, 0);
+        }
+        if (c + 2 < nch) {
+            TDI8_WAIT_LGKM0();
+            __builtin_amdgcn_s_barrier();  // every wave is done with this buffer
+            issue(c + 2);
+        }
+    }
+
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < MT; ++i)
