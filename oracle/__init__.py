@@ -52,12 +52,19 @@ def _load():
         lib.oracle_gemm_elements.restype = None
         lib.oracle_gemm_elements.argtypes = [i64, p, p, i64, p, i64, p, i64, ctypes.c_int, p]
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.restype = None
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = lib
     return _lib
 
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads used by the following calls (OpenMP)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _check_storage(A, B, M, N, K, b_col_major):

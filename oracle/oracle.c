@@ -113,3 +113,13 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Thread count for the following calls (timing on one core or on all). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
