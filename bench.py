@@ -169,6 +169,70 @@ def check_sample(w, A, Bs, C_dev, n=256):
     return bool((got == want).all())
 
 
+REGRET_SHAPES = [(256, 256, 256), (4096, 4096, 4096), (16, 4096, 4096), (1000, 3000, 777),
+                 (16384, 16384, 8192), (2048, 2048, 2048), (8192, 8192, 4096), (1024, 1024, 8192),
+                 (256, 256, 32768), (512, 4096, 4096), (32, 4096, 4096), (16, 8192, 8192),
+                 (4096, 16, 4096), (333, 777, 999)]
+
+
+def selector_report(t):
+    """Time every applicable compiled configuration on a suite of shapes (both
+    B layouts, inputs rotating as in the headline timing), and compare the
+    selection's pick with the fastest.  Every configuration's C must equal
+    the pick's byte for byte.  Prints a markdown table."""
+    import torch
+    torch.manual_seed(0)
+    sh = torch.cuda.current_stream().cuda_stream
+    table = [t.tile_config_info(i) for i in range(t.tile_config_count())]
+    props = torch.cuda.get_device_properties(0)
+    hw = t.HwInfo(props.multi_processor_count, 1024, 256, 32)
+    routes = {t.ROUTE_GENERAL: "", t.ROUTE_FALLBACK: " reuse-1", t.ROUTE_SKINNY: " skinny"}
+    print("| M×N×K | B | selected (route) | selected µs | fastest | fastest µs | regret | configs timed |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (M, N, K) in REGRET_SHAPES:
+        pick = t.select_tile_config(M, N, K)
+        sel = t.select_tile_config_for(M, N, K, hw, [c.blocks_per_cu for c in table])
+        assert sel.id == pick, (M, N, K, sel.id, pick)
+        for bcm in (True, False):
+            w = dict(M=M, N=N, K=K, bcm=bcm)
+            nsets = rotation_sets(w)
+            sets = [(torch.randint(-128, 128, (M, K), dtype=torch.int8, device="cuda"),
+                     torch.randint(-128, 128, (N, K) if bcm else (K, N), dtype=torch.int8, device="cuda"),
+                     torch.empty((M, N), dtype=torch.int32, device="cuda")) for _ in range(nsets)]
+            cands = [c for c in table if c.family == 0 or (M <= c.block_m)]
+            times, ref = {}, None
+            for c in [table[pick]] + [c for c in cands if c.id != pick]:
+                args = [(c.id, int(bcm), M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0),
+                         cc.data_ptr(), cc.stride(0), sh) for (a, b, cc) in sets]
+                t0 = time.perf_counter(); i = 0
+                while time.perf_counter() - t0 < 0.15 or i < nsets:
+                    st = t.gemm_s8s8s32_with_config(*args[i % nsets]); i += 1
+                    assert st == t.OK, t.tdi8_status_string(st)
+                    if i % 64 == 0:
+                        torch.cuda.synchronize()
+                torch.cuda.synchronize()
+                per = (time.perf_counter() - t0) / i
+                n = int(max(5, min(400, 0.1 / max(per, 1e-6))))
+                e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for j in range(n):
+                    t.gemm_s8s8s32_with_config(*args[j % nsets])
+                e1.record(); torch.cuda.synchronize()
+                times[c.id] = e0.elapsed_time(e1) * 1e3 / n
+                # set 0 recomputed by this configuration must match the pick's bytes
+                t.gemm_s8s8s32_with_config(*args[0]); torch.cuda.synchronize()
+                if ref is None:
+                    ref = sets[0][2].clone()
+                else:
+                    assert torch.equal(sets[0][2], ref), f"config {c.id} differs from config {pick} at {M}x{N}x{K}"
+            best = min(times, key=times.get)
+            route = routes.get(sel.route, "")
+            print(f"| {M}×{N}×{K} | {'col' if bcm else 'row'} | {pick}{route} | {times[pick]:.2f} | {best} | "
+                  f"{times[best]:.2f} | {100.0 * (times[pick] / times[best] - 1):.0f}% | {len(times)} |", flush=True)
+            del sets, ref
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -179,6 +243,8 @@ def main():
                     help="B layout of the workload (default: the workload's own; its parity cases use both)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-skinny", action="store_true")
+    ap.add_argument("--selector-report", action="store_true",
+                    help="only time every compiled configuration on a shape suite and print the selector's regret")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (10 times) for counter calibration")
     args = ap.parse_args()
@@ -202,6 +268,9 @@ def main():
         return
     import tiled_dense_int8_amd as t
     torch.cuda.set_device(0)
+    if args.selector_report:
+        selector_report(t)
+        return
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} {props.gcnArchName} CUs={props.multi_processor_count}")
 

@@ -151,6 +151,21 @@ typedef struct {
 int select_tile_config_for(int M, int N, int K, const tdi8_hw_info *hw,
                            const int *blocks_per_cu, tdi8_selection *out);
 
+/* K slices the gemm entry points use with configuration `config_id` for an
+ * M x K by K x N product on a device of `num_cu` compute units, when the
+ * operands take the unpredicated path (sizes multiples of the block tile,
+ * 16-byte aligned pointers, lda and ldb multiples of 16, ldc of 4); other
+ * operands are never split.  Splitting K with integer atomics is the contest
+ * write-up's "Split K" paragraph, added after the five steps of the
+ * selection: while the tiles times twice the slices still fit one block per
+ * compute unit, and each slice stays a whole number of at least four K
+ * tiles, the slices double.  1 = no split (always for the skinny family).
+ * A split call enqueues two kernels on the stream: one zeroes the C window,
+ * the other adds every slice's partial sums into it; the result is the same
+ * bytes as without the split (integer addition in any order).  Host only,
+ * needs no device.  Returns >= 1 or a negative tdi8_status. */
+int tile_config_split_k(int config_id, int M, int N, int K, int num_cu);
+
 /* Host-side argument check shared by every gemm entry point (no device
  * needed): returns TDI8_OK or the status the entry point would return. */
 int tdi8_validate(int b_col_major, int M, int N, int K, const int8_t *A, int lda,

@@ -168,3 +168,19 @@ def test_mi355x_expectations():
     assert s.route == t.ROUTE_SKINNY and tab[s.id].block_m == 16
     s = t.select_tile_config_for(256, 256, 256, hwc, bpc)
     assert s.route == t.ROUTE_FALLBACK and tab[s.id].m_tiles == tab[s.id].n_tiles == 1
+
+
+def test_split_k_matches_oracle_reading():
+    """The library's K-split rule against the oracle's restatement, on a grid
+    of shapes and compute-unit counts (no device needed)."""
+    from oracle.selector import split_k
+    tab = oracle_table([1] * t.tile_config_count())
+    shapes = [(m, n, k) for m in (64, 128, 256, 1024, 4096, 100) for n in (64, 128, 256, 1024, 3000)
+              for k in (128, 256, 512, 768, 1024, 4096, 8192, 32768, 65536, 777)]
+    for num_cu in (256, 120, 304, 8):
+        for c in tab:
+            for (m, n, k) in shapes:
+                assert t.tile_config_split_k(c.id, m, n, k, num_cu) == split_k(c, m, n, k, num_cu), (c.id, m, n, k, num_cu)
+    assert t.tile_config_split_k(-1, 1, 1, 1, 256) == t.ERR_BAD_CONFIG
+    assert t.tile_config_split_k(0, -1, 1, 1, 256) == t.ERR_INVALID_VALUE
+    assert t.tile_config_split_k(0, 1, 1, 1, 0) == t.ERR_INVALID_VALUE

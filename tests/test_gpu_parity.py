@@ -49,6 +49,40 @@ def test_every_config_small_and_ragged(lib, bcm):
 
 
 @pytest.mark.parametrize("bcm", [True, False])
+def test_split_k_every_general_config(lib, bcm):
+    """One tile and a long K: the unpredicated form splits K into slices whose
+    partial sums are added into a zeroed C; bytes must equal the oracle's."""
+    t = lib
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for c in table(t):
+        if c.family != 0:
+            continue
+        for (M, N, K) in [(c.block_m, c.block_n, 32 * c.block_k), (2 * c.block_m, c.block_n, 8 * c.block_k)]:
+            s = t.tile_config_split_k(c.id, M, N, K, cus)
+            assert s >= 2, (c.id, M, N, K, s)
+            A, B = synthetic.gemm_inputs(M, N, K, seed=M + N + K)
+            check_case(DeviceCase(A, B, bcm), f"split-K x{s} cfg{c.id}", config=c.id)
+            # ldc padding must stay untouched by the zeroing kernel
+            check_case(DeviceCase(A, B, bcm, ldc=N + 8), f"split-K x{s} cfg{c.id} ldc+8", config=c.id)
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_split_k_selected_long_k_shapes(lib, bcm):
+    t = lib
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for (M, N, K) in [(256, 256, 32768), (1024, 1024, 8192), (128, 256, 65536), (64, 128, 131072)]:
+        cid = t.select_tile_config(M, N, K)
+        note(f"[info] {M}x{N}x{K} config {cid} splits {t.tile_config_split_k(cid, M, N, K, cus)}")
+        A, B = synthetic.gemm_inputs(M, N, K, seed=11)
+        check_case(DeviceCase(A, B, bcm), "selected long K")
+    # all -128 at K = 131072 wraps to -2^31 exactly; split slices must wrap the same way
+    M, N, K = 64, 128, 131072
+    lo = np.full((M, K), -128, np.int8)
+    lob = np.full((K, N), -128, np.int8)
+    check_case(DeviceCase(lo, lob, bcm), "split wrap", expect=np.full((M, N), -(2 ** 31), np.int32))
+
+
+@pytest.mark.parametrize("bcm", [True, False])
 def test_identity_and_permutation_layout_probe(lib, bcm):
     """A = I gives C = B and A = P gives permuted rows of B: pins the
     accumulator-to-(row, column) map of every configuration."""

@@ -89,3 +89,31 @@ def test_deterministic_and_k_independent():
     a = [select(m, n, 64, HW, table()).id for m in (1, 16, 100, 4096) for n in (1, 300, 4096)]
     b = [select(m, n, 8192, HW, table()).id for m in (1, 16, 100, 4096) for n in (1, 300, 4096)]
     assert a == b
+
+
+def test_split_k_worked_examples():
+    """The K-split rule (a CDNA4 addition after the five steps), worked by hand:
+    slices double while tiles * slices <= #CU and each slice keeps a whole
+    number of at least four K tiles."""
+    from oracle.selector import split_k
+    g64x128 = Cfg(10, "general", 32, 32, 2, 4, 1, 1, 128, 512, 3)       # 64 x 128, BK 128
+    g256 = Cfg(11, "general", 32, 32, 2, 4, 4, 2, 128, 512, 1)          # 256 x 256
+    sk = Cfg(12, "skinny", 16, 16, 1, 1, 1, 1, 2048, 1024, 1)
+    assert (g64x128.BM, g64x128.BN, g256.BM, g256.BN) == (64, 128, 256, 256)
+    # 256x256x32768: 4*2 = 8 tiles; 8*32 = 256 <= 256 and 32768/32 = 1024 >= 512 -> 32
+    assert split_k(g64x128, 256, 256, 32768, 256) == 32
+    # 1024x1024x8192: 16*8 = 128 tiles; 2 slices fill 256 exactly -> 2
+    assert split_k(g64x128, 1024, 1024, 8192, 256) == 2
+    # 4096^3 with 256x256: 256 tiles, no room -> 1
+    assert split_k(g256, 4096, 4096, 4096, 256) == 1
+    # K = 1024: two slices of 512 = 4 tiles of 128; four slices would be 256 -> 2
+    assert split_k(g64x128, 256, 256, 1024, 256) == 2
+    # K = 768: two slices of 384 < 512 -> 1
+    assert split_k(g64x128, 256, 256, 768, 256) == 1
+    # K = 1536: 1536 % 256 == 0 and 768 >= 512 -> 2; 1536 % 512 == 0 but 384 < 512 -> stop
+    assert split_k(g64x128, 256, 256, 1536, 256) == 2
+    # tile-ragged M, the skinny family: never split
+    assert split_k(g64x128, 100, 256, 32768, 256) == 1
+    assert split_k(sk, 16, 4096, 65536, 256) == 1
+    # 120 compute units, 8 tiles: 16 * 8 = 128 > 120 -> 8
+    assert split_k(g64x128, 256, 256, 32768, 120) == 8

@@ -62,6 +62,7 @@ _SIGNATURES = {
     "select_tile_config": (_i, [_i, _i, _i]),
     "tile_config_count": (_i, []),
     "tile_config_info": (_i, [_i, ctypes.POINTER(TileConfig)]),
+    "tile_config_split_k": (_i, [_i, _i, _i, _i, _i]),
     "select_tile_config_for": (_i, [_i, _i, _i, ctypes.POINTER(HwInfo), ctypes.POINTER(_i),
                                     ctypes.POINTER(Selection)]),
     "tdi8_validate": (_i, [_i, _i, _i, _i, _p, _i, _p, _i, _p, _i]),
@@ -102,6 +103,10 @@ def gemm_s8s8s32_with_config(config_id, b_col_major, M, N, K, A, lda, B, ldb, C,
 
 def select_tile_config(M, N, K) -> int:
     return _lib.select_tile_config(M, N, K)
+
+
+def tile_config_split_k(config_id, M, N, K, num_cu) -> int:
+    return _lib.tile_config_split_k(config_id, M, N, K, num_cu)
 
 
 def tile_config_count() -> int:

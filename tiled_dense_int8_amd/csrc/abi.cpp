@@ -15,6 +15,20 @@
 #include "device_common.h"
 
 namespace tdi8 {
+
+// C[0:M, 0:N] = 0 (C 16-byte aligned, ldc and N multiples of 4): run before a
+// K-split launch, whose blocks add their partial sums into C.
+__global__ void __launch_bounds__(256) zero_c_kernel(GemmArgs g) {
+    const int64_t per_row = g.N / 4;
+    const int64_t total = per_row * g.M;
+    for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < total;
+         q += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t m = q / per_row;
+        const int64_t n = 4 * (q - m * per_row);
+        *reinterpret_cast<i32x4 *>(g.C + m * g.ldc + n) = i32x4{0, 0, 0, 0};
+    }
+}
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -113,9 +127,10 @@ DeviceState *current_device(int *status) {
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
-           int32_t *C, int ldc, hipStream_t stream) {
+           int32_t *C, int ldc, hipStream_t stream, int num_cu) {
     const StaticCfg c = static_cfg(id);
     GemmArgs g;
+    g.splits = 1;
     g.A = A;
     g.B = B;
     g.C = C;
@@ -139,6 +154,21 @@ int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, cons
         // both B layouts are moved by 16-byte LDS DMA loads in the fast form
         const bool b_ok = aligned(B, 16) && ldb % 16 == 0;
         fast = M % c.bm == 0 && N % c.bn == 0 && K % c.bk == 0 && a_ok && b_ok && c_ok;
+        if (fast) g.splits = split_k_for(c, M, N, K, num_cu);
+        if (g.splits > 1) {
+            // zero the C window, then one block per tile and K slice adds into it
+            const int64_t quads = static_cast<int64_t>(M) * (N / 4);
+            const unsigned zb = static_cast<unsigned>(quads / 256 + 1 < 2048 ? quads / 256 + 1 : 2048);
+            void *zargs[] = {&g};
+            hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&zero_c_kernel), dim3(zb), dim3(256),
+                                           zargs, 0, stream);
+            if (e != hipSuccess) return hip_fail(e);
+            grid = dim3(static_cast<unsigned>(tm * tn * g.splits));
+            void *args[] = {&g};
+            e = hipLaunchKernel(kernels()[id].split[bcol ? 1 : 0], grid, block, args, 0, stream);
+            if (e != hipSuccess) return hip_fail(e);
+            return TDI8_OK;
+        }
     } else {
         // the unpredicated forms move B by 16-byte LDS DMA loads in both layouts
         fast = M % c.bm == 0 && N % c.bn == 0 && K % c.bk == 0 && a_ok && aligned(B, 16) && ldb % 16 == 0 && c_ok;
@@ -174,7 +204,7 @@ int gemm_entry(int cfg, int bcol, int M, int N, int K, const int8_t *A, int lda,
         id = select_config(M, N, K, ds->hw, ds->bpc, nullptr);
         if (id < 0) return id;
     }
-    return launch(id, bcol, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return launch(id, bcol, M, N, K, A, lda, B, ldb, C, ldc, stream, ds->hw.num_cu);
 }
 
 }  // namespace
@@ -238,6 +268,14 @@ int select_tile_config_for(int M, int N, int K, const tdi8_hw_info *hw, const in
 }
 
 int tile_config_count(void) { return TDI8_NUM_CONFIGS; }
+
+int tile_config_split_k(int config_id, int M, int N, int K, int num_cu) {
+    if (config_id < 0 || config_id >= TDI8_NUM_CONFIGS) return TDI8_ERR_BAD_CONFIG;
+    if (M < 0 || N < 0 || K < 0 || num_cu <= 0) return TDI8_ERR_INVALID_VALUE;
+    const StaticCfg c = static_cfg(config_id);
+    if (c.family != 0 || M % c.bm != 0 || N % c.bn != 0 || K % c.bk != 0) return 1;
+    return split_k_for(c, M, N, K, num_cu);
+}
 
 int tile_config_info(int id, tdi8_tile_config *out) {
     if (id < 0 || id >= TDI8_NUM_CONFIGS) return TDI8_ERR_BAD_CONFIG;

@@ -18,6 +18,7 @@ struct GemmArgs {
     int64_t lda, ldb, ldc;
     int M, N, K;
     int tiles_m, tiles_n;  // block tiles along M and N
+    int splits;            // K slices (1: each block covers all of K)
 };
 
 __device__ __forceinline__ int clamp16(int v) { return v < 0 ? 0 : (v > 16 ? 16 : v); }

@@ -20,7 +20,7 @@ template <class P, bool BCOL, bool FAST>
 static const void *entry() {
     if constexpr (P::family == 0 && FAST)
         return reinterpret_cast<const void *>(
-            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, P::st, !BCOL>);
+            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, P::st, !BCOL, false>);
     else if constexpr (P::family == 0)
         return reinterpret_cast<const void *>(
             &gemm_tiled_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, BCOL, FAST>);
@@ -34,12 +34,23 @@ static const void *entry() {
         return reinterpret_cast<const void *>(&gemm_skinny_rr_kernel<P::mt, P::wk, 2, false>);
 }
 
+template <class P, bool BCOL>
+static const void *split_entry() {
+    if constexpr (P::family == 0)
+        return reinterpret_cast<const void *>(
+            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, P::st, !BCOL, true>);
+    else
+        return nullptr;
+}
+
 void TDI8_CAT(register_cfg_, TDI8_CFG)(KernelSet *ks) {
     using P = CfgParams<TDI8_CFG>;
     ks->kernel[0][0] = entry<P, false, false>();
     ks->kernel[0][1] = entry<P, false, true>();
     ks->kernel[1][0] = entry<P, true, false>();
     ks->kernel[1][1] = entry<P, true, true>();
+    ks->split[0] = split_entry<P, false>();
+    ks->split[1] = split_entry<P, true>();
 }
 
 }  // namespace tdi8

@@ -18,9 +18,12 @@ struct CfgParams;
 TDI8_CONFIG_LIST(TDI8_DEFINE_PARAMS)
 #undef TDI8_DEFINE_PARAMS
 
-// kernel[b_col_major][fast]: host stubs of the four instantiations.
+// kernel[b_col_major][fast]: host stubs of the four instantiations;
+// split[b_col_major]: the K-split form of the fast general kernel (null for
+// the skinny family).
 struct KernelSet {
     const void *kernel[2][2];
+    const void *split[2];
 };
 
 // One registration function per configuration, each defined in its own

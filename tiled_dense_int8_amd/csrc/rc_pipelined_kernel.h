@@ -40,6 +40,16 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // s_waitcnt lgkmcnt(0) with the other counters left at max.
 #define TDI8_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (3 << 14))
 
+// Block barrier that waits on no memory counter (callers first wait for
+// exactly what they need) and that the compiler may not move memory accesses
+// across: the barrier builtin alone is not a memory operation to the
+// optimiser, the empty asm statements with a memory clobber are.
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Tile coordinates of block `bid` in XCD-grouped order.
 __device__ __forceinline__ void tile_of_block(const GemmArgs &g, int bid, int &tm, int &tn) {
     const int total = g.tiles_m * g.tiles_n;
@@ -64,7 +74,10 @@ __device__ __forceinline__ int brow_swizzle(int k) {
     return 2 * ((k / P) % (CPRB / 2));
 }
 
-template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW>
+// SPLIT: the grid holds g.splits blocks per tile, slice s of a tile covering
+// K range [s K / splits, (s + 1) K / splits) and adding its partial sums into
+// C (zeroed beforehand) with integer atomics: exact in any order.
+template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW, bool SPLIT>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArgs g) {
     constexpr int NW = WM * WN;
     constexpr int BM = WM * MF * MT;
@@ -93,11 +106,21 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WN;
     const int wn = wave % WN;
+    int bid = blockIdx.x;
+    int kslice = g.K;    // K extent of this block
+    int64_t k_begin = 0;
+    if constexpr (SPLIT) {
+        const int tiles = g.tiles_m * g.tiles_n;
+        const int slice = bid / tiles;
+        bid -= slice * tiles;
+        kslice = g.K / g.splits;
+        k_begin = static_cast<int64_t>(slice) * kslice;
+    }
     int tm, tn;
-    tile_of_block(g, blockIdx.x, tm, tn);
+    tile_of_block(g, bid, tm, tn);
     const int m0 = tm * BM;
     const int n0 = tn * BN;
-    const int nk = g.K / BK;
+    const int nk = kslice / BK;
 
     // Per-lane source pointers of this wave's load instructions (K offset 0).
     const int8_t *src[LPW];
@@ -107,18 +130,18 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
         if (q < A_CHUNKS) {
             const int r = q / CPR;
             const int c = (q % CPR) ^ chunk_swizzle<CPR>(r);
-            src[i] = g.A + static_cast<int64_t>(m0 + r) * g.lda + 16 * c;
+            src[i] = g.A + static_cast<int64_t>(m0 + r) * g.lda + k_begin + 16 * c;
         } else if constexpr (!BROW) {
             const int qb = q - A_CHUNKS;
             const int r = qb / CPR;
             const int c = (qb % CPR) ^ chunk_swizzle<CPR>(r);
-            src[i] = g.B + static_cast<int64_t>(n0 + r) * g.ldb + 16 * c;
+            src[i] = g.B + static_cast<int64_t>(n0 + r) * g.ldb + k_begin + 16 * c;
         } else {
             // row-major B: LDS row k of the tile holds B(k0 + k, n0 .. n0+BN-1)
             const int qb = q - A_CHUNKS;
             const int k = qb / CPRB;
             const int c = (qb % CPRB) ^ brow_swizzle<BN>(k);
-            src[i] = g.B + static_cast<int64_t>(k) * g.ldb + n0 + 16 * c;
+            src[i] = g.B + (k_begin + k) * g.ldb + n0 + 16 * c;
         }
     }
     // K offset of tile kt for load instruction i.
@@ -254,7 +277,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
                         TDI8_WAIT_VMCNT(0);
                     }
                     TDI8_WAIT_LGKM0();
-                    __builtin_amdgcn_s_barrier();
+                    block_barrier();
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if constexpr (LOAD) {
@@ -289,7 +312,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
             for (int s = 0; s < nk; ++s) issue(s);
             TDI8_WAIT_VMCNT(0);
         }
-        __builtin_amdgcn_s_barrier();
+        block_barrier();
         read_frags(0, 0, 0);
         TDI8_WAIT_LGKM0();  // the K loop starts with no operand read pending
         __builtin_amdgcn_sched_barrier(0);
@@ -305,6 +328,49 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
         // Drain: wait for everything outstanding.
         for (; t + 1 < nk; ++t) tile(t, T0{}, T1{}, T0{});
         tile(t, T0{}, T0{}, T0{});
+    }
+
+    if constexpr (SPLIT) {
+        // Partial sums go through LDS (free once the K loop is done), so that
+        // each atomic instruction covers 64 consecutive columns of one row
+        // (two cache lines) instead of 32 rows.  Rows of the tile are taken
+        // in passes of RP (a multiple of the 32-row instruction tile) that fit
+        // the stage buffers with a 16-byte pad per row (the pad keeps the
+        // 32 rows written by one instruction on different banks).
+        static_assert(MF == 32, "the split epilogue assumes the 32x32 accumulator layout");
+        constexpr int LDS_TOTAL = STAGES * STAGE;
+        constexpr int RS = BN + 4;                                  // int32 per LDS row
+        constexpr int RP0 = (LDS_TOTAL / (RS * 4)) / MF * MF;
+        constexpr int RP = RP0 < BM ? RP0 : BM;
+        static_assert(RP >= MF, "stage buffers hold at least one instruction tile of rows");
+        int32_t *cl = reinterpret_cast<int32_t *>(lds);
+        for (int p0 = 0; p0 < BM; p0 += RP) {
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const int rb = wm * (MT * MF) + i * MF;  // first tile row of this instruction tile
+                if (rb < p0 || rb >= p0 + RP) continue;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int cb = wn * (NT * MF) + j * MF;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int r = rb - p0 + (lane & 31);
+                        const int c = cb + 8 * q + 4 * (lane >> 5);
+                        *reinterpret_cast<i32x4 *>(cl + r * RS + c) =
+                            i32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    }
+                }
+            }
+            __syncthreads();
+            const int rows = BM - p0 < RP ? BM - p0 : RP;
+            for (int idx = threadIdx.x; idx < rows * BN; idx += NW * 64) {
+                const int r = idx / BN;
+                const int c = idx - r * BN;
+                atomicAdd(g.C + static_cast<int64_t>(m0 + p0 + r) * g.ldc + n0 + c, cl[r * RS + c]);
+            }
+        }
+        return;
     }
 
     // Epilogue: lane holds C[m][n .. n+3] per group of four accumulators.

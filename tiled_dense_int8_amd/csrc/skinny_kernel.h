@@ -206,7 +206,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
         } else {
             TDI8_WAIT_VMCNT(0);
         }
-        __builtin_amdgcn_s_barrier();
+        block_barrier();
         const int8_t *b = buf[c & 1];
 #pragma unroll
         for (int kk = 0; kk < KW; kk += 64) {
@@ -224,7 +224,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
         }
         if (c + 2 < nch) {
             TDI8_WAIT_LGKM0();
-            __builtin_amdgcn_s_barrier();  // every wave is done with this buffer
+            block_barrier();  // every wave is done with this buffer
             issue(c + 2);
         }
     }
@@ -349,7 +349,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
         } else {
             TDI8_WAIT_VMCNT(0);
         }
-        __builtin_amdgcn_s_barrier();
+        block_barrier();
         const int8_t *b = buf[c & 1];
 #pragma unroll
         for (int kk = 0; kk < KW; kk += 64) {
@@ -375,7 +375,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
         }
         if (c + 2 < nch) {
             TDI8_WAIT_LGKM0();
-            __builtin_amdgcn_s_barrier();  // every wave is done with this buffer
+            block_barrier();  // every wave is done with this buffer
             issue(c + 2);
         }
     }
