@@ -243,8 +243,8 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
     //  * last step: its operands are already in registers, so first publish
     //    tile t+1 (own DMA loads of t+1 retired, then a barrier: every wave
     //    is done with buffer t % STAGES), refill that buffer with tile
-    //    t+STAGES at once, then the step's matrix work with tile t+1's
-    //    first-step operands read in between.
+    //    t+STAGES, then the step's matrix work with tile t+1's first-step
+    //    operands read in between.
     // Every step ends by retiring its operand reads, so the next step's
     // matrix work starts with its operands in registers.  Issuing a refill
     // right after the barrier that frees its buffer gives it the longest
@@ -280,12 +280,20 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
                     block_barrier();
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                if constexpr (LOAD) {
+                // Row-major B: the refill goes out at once.  Column-major B:
+                // spread over the step's matrix instructions (measured 2%
+                // faster at 16384^2 x 8192, 7% slower with row-major B).
+                if constexpr (LOAD && BROW) {
                     issue(t + STAGES);
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
                 for (int x = 0; x < F; ++x) {
+                    if constexpr (LOAD && !BROW) {
+#pragma unroll
+                        for (int li = 0; li < LPW; ++li)
+                            if ((li * F) / LPW == x) issue_one(t + STAGES, li);
+                    }
                     mma_one(cur, x);
                     if constexpr (NEXT) {
 #pragma unroll
