@@ -77,3 +77,12 @@ def freivalds_vectors(N: int, count: int, seed: int) -> np.ndarray:
     randomised product check C x == A (B x)."""
     v = uniform_int8(count, N, seed, 3).astype(np.int64)
     return v >> 4
+
+
+def conv_inputs(N: int, H: int, W: int, C: int, K: int, R: int, S: int, seed: int):
+    """(x, w) for a convolution: x int8 N x H x W x C (NHWC, stream tag 4) and
+    w int8 K x R x S x C (KRSC, tag 5), uniform over all 256 values, element
+    index = the row-major index of each array."""
+    x = uniform_int8(N * H * W, C, seed, 4).reshape(N, H, W, C)
+    w = uniform_int8(K * R * S, C, seed, 5).reshape(K, R, S, C)
+    return x, w
