@@ -1,0 +1,156 @@
+"""Parity of the implicit-GEMM convolution with the CPU convolution oracle,
+through the C ABI.  Integer work: bit-exact on every compared output.  Small
+shapes are compared in full for every general configuration; the layer shapes
+timed by the bench are compared in full where the oracle is quick, else on
+sampled outputs.  The output buffer carries a sentinel tail that must survive."""
+import numpy as np
+import pytest
+
+import synthetic
+from helpers import note
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+SENT = -123456789
+TAIL = 64
+
+
+@pytest.fixture(scope="module")
+def t():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiled_dense_int8_amd as lib
+    return lib
+
+
+def run_conv(t, x, w, pad, stride, dil, config=None, seed_desc=""):
+    """Device run; returns (y, sentinel tail intact)."""
+    N, H, W, C = x.shape
+    K, R, S, _ = w.shape
+    P = t.conv2d_output_extent(H, R, pad[0], stride[0], dil[0])
+    Q = t.conv2d_output_extent(W, S, pad[1], stride[1], dil[1])
+    note(f"[case] conv N={N} H={H} W={W} C={C} K={K} R={R} S={S} pad={pad} stride={stride} dil={dil} "
+         f"config={config} {seed_desc}")
+    xd = torch.from_numpy(x).cuda()
+    wd = torch.from_numpy(w).cuda()
+    yb = torch.full((N * P * Q * K + TAIL,), SENT, dtype=torch.int32, device="cuda")
+    args = (N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0], dil[1],
+            xd.data_ptr(), wd.data_ptr(), yb.data_ptr(), 0)
+    st = t.conv2d_s8s8s32_nhwc(*args) if config is None else t.conv2d_s8s8s32_nhwc_with_config(config, *args)
+    assert st == t.OK, t.tdi8_status_string(st)
+    torch.cuda.synchronize()
+    flat = yb.cpu().numpy()
+    return flat[:N * P * Q * K].reshape(N, P, Q, K), bool((flat[N * P * Q * K:] == SENT).all())
+
+
+def check(t, shape, pad=(0, 0), stride=(1, 1), dil=(1, 1), config=None, seed=0):
+    import oracle
+    N, H, W, C, K, R, S = shape
+    x, w = synthetic.conv_inputs(N, H, W, C, K, R, S, seed)
+    y, tail_ok = run_conv(t, x, w, pad, stride, dil, config, f"seed={seed}")
+    want = oracle.conv2d(x, w, pad, stride, dil)
+    assert y.shape == want.shape
+    bad = int((y != want).sum())
+    assert bad == 0, f"{bad} mismatches of {want.size}"
+    assert tail_ok, "output tail overwritten"
+
+
+SMALL = [  # (N, H, W, C, K, R, S), pad, stride, dil
+    ((2, 9, 11, 16, 24, 3, 3), (1, 1), (1, 1), (1, 1)),
+    ((1, 13, 7, 32, 70, 3, 3), (0, 2), (2, 1), (1, 1)),
+    ((3, 8, 8, 48, 17, 1, 1), (0, 0), (1, 1), (1, 1)),
+    ((1, 17, 15, 16, 130, 5, 3), (2, 1), (1, 2), (2, 1)),
+    ((2, 6, 6, 64, 9, 7, 7), (3, 3), (1, 1), (1, 1)),
+    ((1, 12, 12, 80, 33, 3, 3), (1, 1), (3, 3), (2, 2)),
+]
+
+
+@pytest.mark.parametrize("case", SMALL)
+def test_every_general_config_small(t, case):
+    shape, pad, stride, dil = case
+    for cid in range(t.tile_config_count()):
+        if t.tile_config_info(cid).family != 0:
+            continue
+        check(t, shape, pad, stride, dil, config=cid, seed=cid)
+
+
+def test_selected_config_shapes(t):
+    for (shape, pad, stride, dil) in SMALL:
+        check(t, shape, pad, stride, dil)
+    # few output pixels, long reduction (the contest's "C*R*S >> M, N" case)
+    check(t, (1, 8, 8, 512, 32, 3, 3), (1, 1))
+    # the whole image is padding for some taps: 1x1 input, 3x3 filter
+    check(t, (4, 1, 1, 16, 8, 3, 3), (1, 1))
+
+
+def test_one_by_one_matches_the_gemm_entry(t):
+    """A 1x1, stride-1 convolution is the product of the (N H W) x C image
+    matrix with the K x C filter matrix (column-major B)."""
+    N, H, W, C, K = 2, 16, 16, 64, 96
+    x, w = synthetic.conv_inputs(N, H, W, C, K, 1, 1, 3)
+    y, _ = run_conv(t, x, w, (0, 0), (1, 1), (1, 1))
+    A = torch.from_numpy(x.reshape(N * H * W, C)).cuda()
+    B = torch.from_numpy(w.reshape(K, C)).cuda()
+    Cg = torch.empty((N * H * W, K), dtype=torch.int32, device="cuda")
+    assert t.gemm_s8s8s32_bt(N * H * W, K, C, A.data_ptr(), C, B.data_ptr(), C, Cg.data_ptr(), K, 0) == t.OK
+    torch.cuda.synchronize()
+    assert np.array_equal(y.reshape(N * H * W, K), Cg.cpu().numpy())
+
+
+def test_edge_cases(t):
+    # C = 0: every output is 0
+    x = np.zeros((2, 4, 4, 0), np.int8)
+    w = np.zeros((5, 3, 3, 0), np.int8)
+    y, tail_ok = run_conv(t, x, w, (1, 1), (1, 1), (1, 1))
+    assert (y == 0).all() and tail_ok
+    # no output position: the dilated filter is larger than the padded image
+    xs, ws = synthetic.conv_inputs(1, 3, 3, 16, 4, 3, 3, 1)
+    yb = torch.full((TAIL,), SENT, dtype=torch.int32, device="cuda")
+    xd = torch.from_numpy(xs).cuda()
+    wd = torch.from_numpy(ws).cuda()
+    assert t.conv2d_output_extent(3, 3, 0, 1, 2) == 0
+    assert t.conv2d_s8s8s32_nhwc(1, 3, 3, 16, 4, 3, 3, 0, 0, 1, 1, 2, 2, xd.data_ptr(), wd.data_ptr(),
+                                 yb.data_ptr(), 0) == t.OK
+    torch.cuda.synchronize()
+    assert (yb.cpu().numpy() == SENT).all()
+    # extremes: all -128, 3x3 with padding: interior outputs are 9 * C * 16384
+    N, H, W, C, K = 1, 6, 6, 32, 8
+    x = np.full((N, H, W, C), -128, np.int8)
+    w = np.full((K, 3, 3, C), -128, np.int8)
+    y, _ = run_conv(t, x, w, (1, 1), (1, 1), (1, 1))
+    assert (y[:, 1:-1, 1:-1, :] == 9 * C * 16384).all() and (y[:, 0, 0, :] == 4 * C * 16384).all()
+
+
+LAYERS = {  # the layer shapes the bench times (see bench.py)
+    "conv3x3_56": ((32, 56, 56, 64, 64, 3, 3), (1, 1), (1, 1)),
+    "conv3x3_14": ((32, 14, 14, 256, 256, 3, 3), (1, 1), (1, 1)),
+    "conv1x1_28": ((32, 28, 28, 256, 512, 1, 1), (0, 0), (1, 1)),
+    "conv3x3_s2": ((32, 56, 56, 128, 128, 3, 3), (1, 1), (2, 2)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LAYERS))
+def test_layer_shapes_sampled(t, name):
+    import oracle
+    shape, pad, stride = LAYERS[name]
+    N, H, W, C, K, R, S = shape
+    x, w = synthetic.conv_inputs(N, H, W, C, K, R, S, 0)
+    y, tail_ok = run_conv(t, x, w, pad, stride, (1, 1))
+    assert tail_ok
+    rng = np.random.default_rng(1)
+    n, p, q, k = (rng.integers(0, d, 4096) for d in y.shape)
+    # plus the borders of the first image, where padding taps are zero
+    P, Q = y.shape[1:3]
+    bp = np.concatenate([np.zeros(Q, int), np.full(Q, P - 1), np.arange(P), np.arange(P)])
+    bq = np.concatenate([np.arange(Q), np.arange(Q), np.zeros(P, int), np.full(P, Q - 1)])
+    n = np.concatenate([n, np.zeros(bp.size, int)])
+    k = np.concatenate([k, rng.integers(0, K, bp.size)])
+    p = np.concatenate([p, bp])
+    q = np.concatenate([q, bq])
+    want = oracle.conv2d_points(x, w, n, p, q, k, pad=pad, stride=stride)
+    assert np.array_equal(y[n, p, q, k], want)
+    # the whole of image 0 against the full oracle
+    full = oracle.conv2d(np.ascontiguousarray(x[:1]), w, pad, stride)
+    assert np.array_equal(y[:1], full)

@@ -66,6 +66,11 @@ _SIGNATURES = {
     "select_tile_config_for": (_i, [_i, _i, _i, ctypes.POINTER(HwInfo), ctypes.POINTER(_i),
                                     ctypes.POINTER(Selection)]),
     "tdi8_validate": (_i, [_i, _i, _i, _i, _p, _i, _p, _i, _p, _i]),
+    "conv2d_s8s8s32_nhwc": (_i, [_i] * 13 + [_p, _p, _p, _p]),
+    "conv2d_s8s8s32_nhwc_with_config": (_i, [_i] * 14 + [_p, _p, _p, _p]),
+    "conv2d_select_config": (_i, [_i] * 13),
+    "conv2d_output_extent": (_i, [_i] * 5),
+    "conv2d_validate": (_i, [_i] * 13 + [_p, _p, _p]),
     "tdi8_status_string": (ctypes.c_char_p, [_i]),
     "tdi8_last_hip_error": (_i, []),
 }
@@ -180,6 +185,52 @@ def gemm(A: "torch.Tensor", B: "torch.Tensor", b_col_major: bool, out: "torch.Te
     else:
         st = gemm_s8s8s32_with_config(config, b_col_major, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
                                       out.data_ptr(), ldc, s)
+    if st != OK:
+        raise TDI8Error(st)
+    return out
+
+
+# ---- convolution ---------------------------------------------------------------
+
+def conv2d_s8s8s32_nhwc(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w,
+                        x, w, y, stream=0) -> int:
+    return _lib.conv2d_s8s8s32_nhwc(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w,
+                                    x, w, y, stream)
+
+
+def conv2d_s8s8s32_nhwc_with_config(config_id, N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w,
+                                    dil_h, dil_w, x, w, y, stream=0) -> int:
+    return _lib.conv2d_s8s8s32_nhwc_with_config(config_id, N, H, W, C, K, R, S, pad_h, pad_w, stride_h,
+                                                stride_w, dil_h, dil_w, x, w, y, stream)
+
+
+def conv2d_select_config(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w) -> int:
+    return _lib.conv2d_select_config(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w)
+
+
+def conv2d_output_extent(H, R, pad, stride, dil) -> int:
+    return _lib.conv2d_output_extent(H, R, pad, stride, dil)
+
+
+def conv2d_validate(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, x, w, y) -> int:
+    return _lib.conv2d_validate(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, x, w, y)
+
+
+def conv2d(x, w, pad=(0, 0), stride=(1, 1), dil=(1, 1), out=None, config=None, stream=None):
+    """y = conv2d(x, w) for torch tensors on the GPU: x int8 N x H x W x C,
+    w int8 K x R x S x C (both contiguous), y int32 N x P x Q x K."""
+    N, H, W, C = x.shape
+    K, R, S, _ = w.shape
+    P = conv2d_output_extent(H, R, pad[0], stride[0], dil[0])
+    Q = conv2d_output_extent(W, S, pad[1], stride[1], dil[1])
+    if P < 0 or Q < 0:
+        raise TDI8Error(min(P, Q))
+    if out is None:
+        out = torch.empty((N, P, Q, K), dtype=torch.int32, device=x.device)
+    sh = torch.cuda.current_stream().cuda_stream if stream is None else stream
+    args = (N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0], dil[1],
+            x.data_ptr(), w.data_ptr(), out.data_ptr(), sh)
+    st = conv2d_s8s8s32_nhwc(*args) if config is None else conv2d_s8s8s32_nhwc_with_config(config, *args)
     if st != OK:
         raise TDI8Error(st)
     return out

@@ -207,6 +207,85 @@ int gemm_entry(int cfg, int bcol, int M, int N, int K, const int8_t *A, int lda,
     return launch(id, bcol, M, N, K, A, lda, B, ldb, C, ldc, stream, ds->hw.num_cu);
 }
 
+int64_t conv_extent(int64_t H, int64_t R, int64_t pad, int64_t stride, int64_t dil) {
+    const int64_t span = H + 2 * pad - dil * (R - 1) - 1;
+    return span < 0 ? 0 : span / stride + 1;
+}
+
+struct ConvShape {
+    int N, H, W, C, K, R, S, ph, pw, sh, sw, dh, dw;
+};
+
+// Host checks of a convolution call; fills the GEMM view and the geometry.
+int conv_check(const ConvShape &c, const int8_t *x, const int8_t *w, const int32_t *y, GemmArgs *g,
+               ConvParams *cv) {
+    if (c.N < 0 || c.H < 0 || c.W < 0 || c.C < 0 || c.K < 0 || c.R < 1 || c.S < 1 || c.ph < 0 || c.pw < 0 ||
+        c.sh < 1 || c.sw < 1 || c.dh < 1 || c.dw < 1)
+        return TDI8_ERR_INVALID_VALUE;
+    if (c.C % 16 != 0) return TDI8_ERR_INVALID_VALUE;
+    const int64_t P = conv_extent(c.H, c.R, c.ph, c.sh, c.dh);
+    const int64_t Q = conv_extent(c.W, c.S, c.pw, c.sw, c.dw);
+    const int64_t M = static_cast<int64_t>(c.N) * P * Q;
+    const int64_t rsc = static_cast<int64_t>(c.R) * c.S * c.C;
+    if (M > INT_MAX || rsc > INT_MAX || P > INT_MAX || Q > INT_MAX) return TDI8_ERR_INVALID_VALUE;
+    g->A = x;
+    g->B = w;
+    g->C = const_cast<int32_t *>(y);
+    g->lda = 0;
+    g->ldb = rsc;
+    g->ldc = c.K;
+    g->M = static_cast<int>(M);
+    g->N = c.K;
+    g->K = static_cast<int>(rsc);
+    g->splits = 1;
+    *cv = ConvParams{c.N, c.H, c.W, c.C, c.R, c.S, static_cast<int>(P), static_cast<int>(Q),
+                     c.sh, c.sw, c.ph, c.pw, c.dh, c.dw, static_cast<int>(rsc)};
+    if (M == 0 || c.K == 0) return TDI8_OK;
+    if (!y) return TDI8_ERR_NULL_POINTER;
+    if (!aligned(y, 4)) return TDI8_ERR_INVALID_VALUE;
+    if (rsc == 0) return TDI8_OK;
+    if (!x || !w) return TDI8_ERR_NULL_POINTER;
+    if (!aligned(x, 16) || !aligned(w, 16)) return TDI8_ERR_INVALID_VALUE;
+    const uintptr_t y0 = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t y1 = y0 + 4 * static_cast<uint64_t>(M) * static_cast<uint64_t>(c.K);
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(x);
+    const uintptr_t x1 = x0 + static_cast<uint64_t>(c.N) * c.H * c.W * c.C;
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(w);
+    const uintptr_t w1 = w0 + static_cast<uint64_t>(c.K) * static_cast<uint64_t>(rsc);
+    if (overlaps(y0, y1, x0, x1) || overlaps(y0, y1, w0, w1)) return TDI8_ERR_ALIASING;
+    return TDI8_OK;
+}
+
+int conv_entry(int cfg, const ConvShape &c, const int8_t *x, const int8_t *w, int32_t *y, hipStream_t stream) {
+    GemmArgs g;
+    ConvParams cv;
+    int st = conv_check(c, x, w, y, &g, &cv);
+    if (st != TDI8_OK) return st;
+    if (cfg >= TDI8_NUM_CONFIGS || cfg < -1) return TDI8_ERR_BAD_CONFIG;
+    if (g.M == 0 || g.N == 0) return TDI8_OK;
+    DeviceState *ds = current_device(&st);
+    if (!ds) return st;
+    int id = cfg;
+    if (id < 0) {
+        tdi8_hw_info hw = ds->hw;
+        hw.skinny_max_m = 0;  // the convolution form exists for the general family only
+        id = select_config(g.M, g.N, g.K, hw, ds->bpc, nullptr);
+        if (id < 0) return id;
+    }
+    const StaticCfg sc = static_cfg(id);
+    if (sc.family != 0) return TDI8_ERR_BAD_CONFIG;
+    const int64_t tm = (g.M + static_cast<int64_t>(sc.bm) - 1) / sc.bm;
+    const int64_t tn = (g.N + static_cast<int64_t>(sc.bn) - 1) / sc.bn;
+    if (tm * tn > INT_MAX / sc.threads) return TDI8_ERR_INVALID_VALUE;
+    g.tiles_m = static_cast<int>(tm);
+    g.tiles_n = static_cast<int>(tn);
+    void *args[] = {&g, &cv};
+    hipError_t e = hipLaunchKernel(kernels()[id].conv, dim3(static_cast<unsigned>(tm * tn)), dim3(sc.threads), args,
+                                   0, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return TDI8_OK;
+}
+
 }  // namespace
 }  // namespace tdi8
 
@@ -268,6 +347,50 @@ int select_tile_config_for(int M, int N, int K, const tdi8_hw_info *hw, const in
 }
 
 int tile_config_count(void) { return TDI8_NUM_CONFIGS; }
+
+int conv2d_output_extent(int H, int R, int pad, int stride, int dil) {
+    if (H < 0 || R < 1 || pad < 0 || stride < 1 || dil < 1) return TDI8_ERR_INVALID_VALUE;
+    const int64_t e = conv_extent(H, R, pad, stride, dil);
+    return e > INT_MAX ? TDI8_ERR_INVALID_VALUE : static_cast<int>(e);
+}
+
+int conv2d_validate(int N, int H, int W, int C, int K, int R, int S, int pad_h, int pad_w, int stride_h,
+                    int stride_w, int dil_h, int dil_w, const int8_t *x, const int8_t *w, const int32_t *y) {
+    GemmArgs g;
+    ConvParams cv;
+    return conv_check(ConvShape{N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w}, x, w, y,
+                      &g, &cv);
+}
+
+int conv2d_s8s8s32_nhwc(int N, int H, int W, int C, int K, int R, int S, int pad_h, int pad_w, int stride_h,
+                        int stride_w, int dil_h, int dil_w, const int8_t *x, const int8_t *w, int32_t *y,
+                        hipStream_t stream) {
+    return conv_entry(-1, ConvShape{N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w}, x, w,
+                      y, stream);
+}
+
+int conv2d_s8s8s32_nhwc_with_config(int config_id, int N, int H, int W, int C, int K, int R, int S, int pad_h,
+                                    int pad_w, int stride_h, int stride_w, int dil_h, int dil_w, const int8_t *x,
+                                    const int8_t *w, int32_t *y, hipStream_t stream) {
+    if (config_id < 0 || config_id >= TDI8_NUM_CONFIGS) return TDI8_ERR_BAD_CONFIG;
+    return conv_entry(config_id, ConvShape{N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w},
+                      x, w, y, stream);
+}
+
+int conv2d_select_config(int N, int H, int W, int C, int K, int R, int S, int pad_h, int pad_w, int stride_h,
+                         int stride_w, int dil_h, int dil_w) {
+    GemmArgs g;
+    ConvParams cv;
+    const int st = conv_check(ConvShape{N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w},
+                              nullptr, nullptr, nullptr, &g, &cv);
+    if (st != TDI8_OK && st != TDI8_ERR_NULL_POINTER) return st;
+    int s2 = TDI8_OK;
+    DeviceState *ds = current_device(&s2);
+    if (!ds) return s2;
+    tdi8_hw_info hw = ds->hw;
+    hw.skinny_max_m = 0;
+    return select_config(g.M, g.N, g.K, hw, ds->bpc, nullptr);
+}
 
 int tile_config_split_k(int config_id, int M, int N, int K, int num_cu) {
     if (config_id < 0 || config_id >= TDI8_NUM_CONFIGS) return TDI8_ERR_BAD_CONFIG;

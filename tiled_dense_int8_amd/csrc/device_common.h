@@ -21,6 +21,15 @@ struct GemmArgs {
     int splits;            // K slices (1: each block covers all of K)
 };
 
+// Convolution geometry (NHWC image, KRSC filters): image N x H x W x C,
+// filters R x S, output P x Q, stride sh/sw, zero padding ph/pw, dilation
+// dh/dw; rsc = R * S * C, the reduction length.
+struct ConvParams {
+    int N, H, W, C, R, S, P, Q;
+    int sh, sw, ph, pw, dh, dw;
+    int rsc;
+};
+
 __device__ __forceinline__ int clamp16(int v) { return v < 0 ? 0 : (v > 16 ? 16 : v); }
 __device__ __forceinline__ int clamp4(int v) { return v < 0 ? 0 : (v > 4 ? 4 : v); }
 

@@ -43,6 +43,14 @@ static const void *split_entry() {
         return nullptr;
 }
 
+template <class P>
+static const void *conv_entry() {
+    if constexpr (P::family == 0)
+        return reinterpret_cast<const void *>(&conv_implicit_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, P::st>);
+    else
+        return nullptr;
+}
+
 void TDI8_CAT(register_cfg_, TDI8_CFG)(KernelSet *ks) {
     using P = CfgParams<TDI8_CFG>;
     ks->kernel[0][0] = entry<P, false, false>();
@@ -51,6 +59,7 @@ void TDI8_CAT(register_cfg_, TDI8_CFG)(KernelSet *ks) {
     ks->kernel[1][1] = entry<P, true, true>();
     ks->split[0] = split_entry<P, false>();
     ks->split[1] = split_entry<P, true>();
+    ks->conv = conv_entry<P>();
 }
 
 }  // namespace tdi8

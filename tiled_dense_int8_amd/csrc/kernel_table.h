@@ -20,10 +20,11 @@ TDI8_CONFIG_LIST(TDI8_DEFINE_PARAMS)
 
 // kernel[b_col_major][fast]: host stubs of the four instantiations;
 // split[b_col_major]: the K-split form of the fast general kernel (null for
-// the skinny family).
+// the skinny family); conv: the implicit-GEMM convolution form.
 struct KernelSet {
     const void *kernel[2][2];
     const void *split[2];
+    const void *conv;   // implicit-GEMM convolution form (null for the skinny family)
 };
 
 // One registration function per configuration, each defined in its own

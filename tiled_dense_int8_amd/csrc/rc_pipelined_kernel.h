@@ -50,6 +50,10 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Sixteen zero bytes in device memory: the DMA source of chunks that lie
+// outside the operand (zero padding of the convolution, K and row tails).
+static __device__ __attribute__((aligned(16))) const int8_t zero_chunk[16] = {};
+
 // Tile coordinates of block `bid` in XCD-grouped order.
 __device__ __forceinline__ void tile_of_block(const GemmArgs &g, int bid, int &tm, int &tn) {
     const int total = g.tiles_m * g.tiles_n;
@@ -77,8 +81,9 @@ __device__ __forceinline__ int brow_swizzle(int k) {
 // SPLIT: the grid holds g.splits blocks per tile, slice s of a tile covering
 // K range [s K / splits, (s + 1) K / splits) and adding its partial sums into
 // C (zeroed beforehand) with integer atomics: exact in any order.
-template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW, bool SPLIT>
-__global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArgs g) {
+template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW, bool SPLIT, int SRC>
+__device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvParams &cv) {
+    static_assert(SRC == 0 || (!BROW && !SPLIT), "the convolution source is column-major B, unsplit");
     constexpr int NW = WM * WN;
     constexpr int BM = WM * MF * MT;
     constexpr int BN = WN * MF * NT;
@@ -120,13 +125,44 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
     tile_of_block(g, bid, tm, tn);
     const int m0 = tm * BM;
     const int n0 = tn * BN;
-    const int nk = kslice / BK;
+    // GEMM: K is a multiple of BK.  Convolution: the reduction R*S*C is a
+    // multiple of 16 and its last K tile is completed with zero chunks.
+    const int nk = SRC == 0 ? kslice / BK : (cv.rsc + BK - 1) / BK;
 
     // Per-lane source pointers of this wave's load instructions (K offset 0).
     const int8_t *src[LPW];
+    // Convolution: per load slot, the row's base (image or filter), the
+    // image position of tap (0, 0), the 16-byte chunk of the K tile, and
+    // whether the row exists (output pixel < M, output channel < N).
+    [[maybe_unused]] int cih[LPW], ciw[LPW], cch[LPW];
+    [[maybe_unused]] bool cok[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int q = (i * NW + wave) * 64 + lane;
+        if constexpr (SRC == 1) {
+            const bool is_a = q < A_CHUNKS;
+            const int qq = is_a ? q : q - A_CHUNKS;
+            const int r = qq / CPR;
+            cch[i] = (qq % CPR) ^ chunk_swizzle<CPR>(r);
+            if (is_a) {
+                const int m = m0 + r;
+                cok[i] = m < g.M;
+                const int mm = cok[i] ? m : 0;
+                const int img = mm / (cv.P * cv.Q);
+                const int pq = mm - img * (cv.P * cv.Q);
+                const int p = pq / cv.Q;
+                const int qc = pq - p * cv.Q;
+                cih[i] = p * cv.sh - cv.ph;
+                ciw[i] = qc * cv.sw - cv.pw;
+                src[i] = g.A + static_cast<int64_t>(img) * cv.H * cv.W * cv.C;
+            } else {
+                const int n = n0 + r;
+                cok[i] = n < g.N;
+                cih[i] = ciw[i] = 0;
+                src[i] = g.B + static_cast<int64_t>(cok[i] ? n : 0) * g.ldb;
+            }
+            continue;
+        }
         if (q < A_CHUNKS) {
             const int r = q / CPR;
             const int c = (q % CPR) ^ chunk_swizzle<CPR>(r);
@@ -149,9 +185,30 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
         const bool is_b = (i * NW + wave) * 64 >= A_CHUNKS;
         return (BROW && is_b) ? static_cast<int64_t>(kt) * BK * g.ldb : static_cast<int64_t>(kt) * BK;
     };
+    // Source of load slot i for K tile kt.
+    auto source = [&](int i, int kt) -> const int8_t * {
+        if constexpr (SRC == 0) {
+            return src[i] + koff(i, kt);
+        } else {
+            const bool is_a = (i * NW + wave) * 64 < A_CHUNKS;
+            const int kpos = kt * BK + 16 * cch[i];
+            if (!cok[i] || kpos >= cv.rsc) return zero_chunk;
+            if (!is_a) return src[i] + kpos;
+            const int rs = kpos / cv.C;
+            const int c0 = kpos - rs * cv.C;
+            const int r = rs / cv.S;
+            const int ss = rs - r * cv.S;
+            const int ih = cih[i] + r * cv.dh;
+            const int iw = ciw[i] + ss * cv.dw;
+            if (static_cast<unsigned>(ih) >= static_cast<unsigned>(cv.H) ||
+                static_cast<unsigned>(iw) >= static_cast<unsigned>(cv.W))
+                return zero_chunk;
+            return src[i] + (static_cast<int64_t>(ih) * cv.W + iw) * cv.C + c0;
+        }
+    };
     auto issue_one = [&](int kt, int i) {
         int8_t *dst = lds + (kt % STAGES) * STAGE + (i * NW + wave) * 1024;
-        __builtin_amdgcn_global_load_lds(src[i] + koff(i, kt), (lds_void_t *)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(source(i, kt), (lds_void_t *)dst, 16, 0, 0);
     };
     auto issue = [&](int kt) {
 #pragma unroll
@@ -394,14 +451,32 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
                 for (int q = 0; q < 4; ++q) {
                     const int n = nb + 8 * q + 4 * (lane >> 5);
                     i32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    store4<true>(g, m, n, v);
+                    store4<SRC == 0>(g, m, n, v);
                 }
             } else {
-                store4<true>(g, mb + (lane & 15), nb + 4 * (lane >> 4), acc[i][j]);
+                store4<SRC == 0>(g, mb + (lane & 15), nb + 4 * (lane >> 4), acc[i][j]);
             }
         }
     }
 #endif
+}
+
+template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW, bool SPLIT>
+__global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArgs g) {
+    pipelined_body<MF, WM, WN, MT, NT, BK, STAGES, BROW, SPLIT, 0>(g, ConvParams{});
+}
+
+// Implicit-GEMM convolution ("先导杯比赛回顾", 卷积转化: the convolution
+// lowered to a matrix product, here without materialising the im2col
+// matrix): A row m = output pixel (n, p, q) of an NHWC image, A column
+// (r, s, c) = the input byte the im2col index map picks, B = the KRSC filter
+// bank read as a column-major K x (R S C) matrix, C = the N P Q x K output.
+// Every 16-byte A chunk is 16 channels of one tap, gathered straight into LDS
+// by the same DMA loads; taps outside the image, the K tail past R S C and
+// rows past M or N read a zero chunk instead.
+template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES>
+__global__ void __launch_bounds__(WM * WN * 64) conv_implicit_kernel(GemmArgs g, ConvParams cv) {
+    pipelined_body<MF, WM, WN, MT, NT, BK, STAGES, false, false, 1>(g, cv);
 }
 
 }  // namespace tdi8
