@@ -41,6 +41,16 @@ WORKLOADS = {
 }
 
 
+# int8 convolution layers (NHWC image, KRSC filters; typical CNN inference
+# shapes, no dataset): (N, H, W, C, K, R, S), (pad_h, pad_w), (stride_h, stride_w)
+CONV_WORKLOADS = {
+    "conv3x3_56": ((32, 56, 56, 64, 64, 3, 3), (1, 1), (1, 1)),
+    "conv3x3_14": ((32, 14, 14, 256, 256, 3, 3), (1, 1), (1, 1)),
+    "conv1x1_28": ((32, 28, 28, 256, 512, 1, 1), (0, 0), (1, 1)),
+    "conv3x3_s2": ((32, 56, 56, 128, 128, 3, 3), (1, 1), (2, 2)),
+}
+
+
 def log(msg: str) -> None:
     sys.stderr.write(msg + "\n")
     sys.stderr.flush()
@@ -169,6 +179,69 @@ def check_sample(w, A, Bs, C_dev, n=256):
     return bool((got == want).all())
 
 
+def conv_bench(t, name, steps, warmup):
+    """One JSON line for an int8 convolution layer: TOPS and the roofline
+    (MFMA or HBM by the layer's intensity), cold (rotating input sets)."""
+    import torch
+    import numpy as np
+    import oracle
+    import synthetic
+    (N, H, W, C, K, R, S), pad, stride = CONV_WORKLOADS[name]
+    P = t.conv2d_output_extent(H, R, pad[0], stride[0], 1)
+    Q = t.conv2d_output_extent(W, S, pad[1], stride[1], 1)
+    x, w = synthetic.conv_inputs(N, H, W, C, K, R, S, 0)
+    ops = 2.0 * N * P * Q * K * R * S * C
+    byts = x.size + w.size + 4 * N * P * Q * K
+    nsets = max(2, min(64, -(-3 * MALL_BYTES // byts)))
+    xd = torch.from_numpy(x).cuda()
+    wd = torch.from_numpy(w).cuda()
+    sets = [(xd if i == 0 else xd.clone(), wd if i == 0 else wd.clone(),
+             torch.empty((N, P, Q, K), dtype=torch.int32, device="cuda")) for i in range(nsets)]
+    sh = torch.cuda.current_stream().cuda_stream
+    args = [(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], 1, 1, a.data_ptr(), b.data_ptr(),
+             c.data_ptr(), sh) for (a, b, c) in sets]
+    for i in range(warmup):
+        st = t.conv2d_s8s8s32_nhwc(*args[i % nsets])
+        assert st == t.OK, t.tdi8_status_string(st)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(steps):
+        t.conv2d_s8s8s32_nhwc(*args[i % nsets])
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    kern_ms = ev0.elapsed_time(ev1) / steps
+    rng = np.random.default_rng(1)
+    idx = [rng.integers(0, d, 512) for d in (N, P, Q, K)]
+    y = sets[(steps - 1) % nsets][2].cpu().numpy()
+    ok = bool(np.array_equal(y[tuple(idx)], oracle.conv2d_points(x, w, *idx, pad=pad, stride=stride)))
+    cfg = t.conv2d_select_config(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], 1, 1)
+    info = t.tile_config_info(cfg)
+    intensity = ops / byts
+    if intensity >= MFMA_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(ops / (kern_ms * 1e-3) / 1e12, 3), "peak": MFMA_PEAK_TOPS,
+                "unit": "TOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(byts / (kern_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    log(f"[bench] {name}: config {cfg} wall {wall_ms * 1e3:.2f} us, kernel {kern_ms * 1e3:.2f} us, "
+        f"{ops / (kern_ms * 1e-3) / 1e12:.1f} TOPS, {byts / (kern_ms * 1e-3) / 1e9:.0f} GB/s, sample parity {ok}")
+    return {"metric": "INT8 convolution TOPS (int32 acc), implicit GEMM", "value": round(ops / (wall_ms * 1e-3) / 1e12, 3),
+            "unit": "TOPS", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(wall_ms, 6),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+            "config": {"workload": f"int8 conv2d N={N} H={H} W={W} C={C} K={K} R={R} S={S} pad={list(pad)} "
+                                   f"stride={list(stride)}, x NHWC, w KRSC, y NPQK int32",
+                       "tile_config": cfg, "block_tile": [info.block_m, info.block_n, info.block_k],
+                       "gemm_view": [N * P * Q, K, R * S * C], "rotating_input_sets": nsets, "sample_parity": ok,
+                       "intensity_ops_per_byte": round(intensity, 1)},
+            "roofline": roof}
+
+
 REGRET_SHAPES = [(256, 256, 256), (4096, 4096, 4096), (16, 4096, 4096), (1000, 3000, 777),
                  (16384, 16384, 8192), (2048, 2048, 2048), (8192, 8192, 4096), (1024, 1024, 8192),
                  (256, 256, 32768), (512, 4096, 4096), (32, 4096, 4096), (16, 8192, 8192),
@@ -238,7 +311,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="square4096", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="square4096", choices=sorted(WORKLOADS) + sorted(CONV_WORKLOADS))
     ap.add_argument("--layout", default=None, choices=["col", "row"],
                     help="B layout of the workload (default: the workload's own; its parity cases use both)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -270,6 +343,9 @@ def main():
     torch.cuda.set_device(0)
     if args.selector_report:
         selector_report(t)
+        return
+    if args.workload in CONV_WORKLOADS:
+        print(json.dumps(conv_bench(t, args.workload, args.steps, args.warmup)), flush=True)
         return
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} {props.gcnArchName} CUs={props.multi_processor_count}")

@@ -49,6 +49,10 @@ Readings:
   claim 6: Launch_kernel_times = ceil(Thread_Blocks / (num_cu * blocks_per_cu)),
       the number of rounds of resident blocks.  Step 5 keeps the minimum.
   Remaining ties: first in table order.
+  step 1 on CDNA4 (an addition, not in the claims): a configuration whose
+      block tile overhangs the problem (BM above max(m, the family's smallest
+      BM), or BN likewise) only adds zero rows or columns and is left out, at
+      step 1 and among the fallback's reuse-1 siblings, unless none is left.
 """
 from __future__ import annotations
 
@@ -173,10 +177,21 @@ def split_k(c: Cfg, m: int, n: int, k: int, num_cu: int) -> int:
     return best
 
 
+def no_overhang(cands: list[Cfg], m: int, n: int, table: list[Cfg]) -> list[Cfg]:
+    """CDNA4 addition to step 1: keep the configurations whose block tile is
+    no taller than max(m, smallest block height of the general family) and
+    no wider than max(n, smallest width); all of them if none is."""
+    gen = [c for c in table if c.family == "general"]
+    hmin = min(c.BM for c in gen)
+    wmin = min(c.BN for c in gen)
+    fit = [c for c in cands if c.BM <= max(m, hmin) and c.BN <= max(n, wmin)]
+    return fit if fit else list(cands)
+
+
 def select(m: int, n: int, k: int, hw: Hw, table: list[Cfg]) -> Result:
     """Pick a configuration id for an m x k times k x n product."""
     trace: dict = {}
-    general = [c for c in table if c.family == "general"]
+    general = no_overhang([c for c in table if c.family == "general"], m, n, table)
     trace["step1"] = [c.id for c in general]
     s2 = [c for c in general if step2_ok(c, hw)]
     trace["step2"] = [c.id for c in s2]
@@ -192,7 +207,7 @@ def select(m: int, n: int, k: int, hw: Hw, table: list[Cfg]) -> Result:
             if d is not None and d.id not in seen and step2_ok(d, hw):
                 seen.add(d.id)
                 s3.append(d)
-        s3.sort(key=lambda c: c.id)
+        s3 = no_overhang(sorted(s3, key=lambda c: c.id), m, n, table)
         if m <= hw.skinny_max_m:
             skinny = [c for c in table if c.family == "skinny" and c.BM >= m and step2_ok(c, hw)]
             if skinny:

@@ -53,8 +53,10 @@ def test_derived_quantities():
     (16, 8192, 7, 2),
     # 17 x 4096: smallest skinny BM >= 17 is 32 -> id8 (256 blocks)
     (17, 4096, 8, 2),
-    # 33 x 4096: too tall for the skinny family -> fallback siblings {2, 5} -> id2
-    (33, 4096, 2, 1),
+    # 33 x 4096: step 1 keeps block heights <= max(33, 32) = 33, i.e. only id5 (32 x 32);
+    # 2 * 128 = 256 < 8 * 256 blocks -> fallback; id5 is its own reuse-1 sibling; too tall
+    # for the skinny family -> id5
+    (33, 4096, 5, 1),
     # 1 x 1: fallback then skinny; nothing fills, keep {6, 7}; ratio picks id7
     (1, 1, 7, 2),
 ])
@@ -80,9 +82,25 @@ def test_other_hardware():
     r = select(4096, 4096, 4096, Hw(num_cu=304), table())
     assert r.id == 1 and r.route == 0
     # 256-thread blocks only: the 512-thread skinny kernels are excluded, so 16 x 4096 stays
-    # on the reuse-1 fallback -> {2, 5} -> id2
+    # on the reuse-1 fallback; step 1 kept only id5 (block height 32 <= max(16, 32)) -> id5
     r = select(16, 4096, 4096, Hw(max_threads_per_block=256), table())
-    assert (r.id, r.route) == (2, 1)
+    assert (r.id, r.route) == (5, 1)
+
+
+def test_no_overhang_step1():
+    """The CDNA4 addition to step 1, worked by hand on the fake table
+    (smallest block height and width 32)."""
+    # m = 4096, n = 64: widths <= 64 survive: id2 (64 x 64), id3 (128 x 64), id5 (32 x 32);
+    # id3: 32 * 1 = 32 blocks < 2 * 256, id2 64 < 4 * 256, id5 256 < 8 * 256 -> fallback;
+    # siblings {2, 5} (of 2, 3 and 5), both fit; ratio 32 > 16 -> id2
+    r = select(4096, 64, 4096, HW, table())
+    assert r.trace["step1"] == [2, 3, 5] and (r.id, r.route) == (2, 1)
+    # m = 100, n = 100: heights and widths <= 100: id2 and id5 -> fallback -> id2
+    r = select(100, 100, 4096, HW, table())
+    assert r.trace["step1"] == [2, 5] and r.id == 2
+    # m = 8, n = 8: nothing is within max(8, 32) = 32 but id5 -> id5 survives step 1
+    r = select(8, 8, 4096, Hw(skinny_max_m=0), table())
+    assert r.trace["step1"] == [5] and (r.id, r.route) == (5, 1)
 
 
 def test_deterministic_and_k_independent():

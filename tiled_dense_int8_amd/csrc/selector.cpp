@@ -104,12 +104,30 @@ int select_config(int M, int N, int K, const tdi8_hw_info &hw, const int *bpc, t
     Cand list[TDI8_NUM_CONFIGS];
     int count[5] = {0, 0, 0, 0, 0};
 
-    // Steps 1 and 2.
+    // Step 1: the general configurations whose block tile does not overhang
+    // the problem (block height at most max(M, smallest height in the list),
+    // width likewise; a CDNA4 addition: a larger block only adds zero rows
+    // or columns), or all of them if none qualifies.  Then step 2.
+    int min_bm = 0, min_bn = 0;
+    for (int id = 0; id < TDI8_NUM_CONFIGS; ++id) {
+        const StaticCfg c = static_cfg(id);
+        if (c.family != 0) continue;
+        if (min_bm == 0 || c.bm < min_bm) min_bm = c.bm;
+        if (min_bn == 0 || c.bn < min_bn) min_bn = c.bn;
+    }
+    auto fits = [&](const StaticCfg &c) {
+        return c.bm <= (M > min_bm ? M : min_bm) && c.bn <= (N > min_bn ? N : min_bn);
+    };
+    bool any_fit = false;
+    for (int id = 0; id < TDI8_NUM_CONFIGS; ++id) {
+        const StaticCfg c = static_cfg(id);
+        if (c.family == 0 && fits(c)) any_fit = true;
+    }
     Cand s2[TDI8_NUM_CONFIGS];
     int n2 = 0;
     for (int id = 0; id < TDI8_NUM_CONFIGS; ++id) {
         const StaticCfg c = static_cfg(id);
-        if (c.family != 0) continue;
+        if (c.family != 0 || (any_fit && !fits(c))) continue;
         ++count[0];
         if (passes_step2(c, bpc[id], hw)) s2[n2++] = Cand{c, bpc[id]};
     }
@@ -128,8 +146,11 @@ int select_config(int M, int N, int K, const tdi8_hw_info &hw, const int *bpc, t
             const int r = s2[i].c.reuse1_id;
             if (r >= 0 && !taken[r] && passes_step2(static_cfg(r), bpc[r], hw)) taken[r] = true;
         }
+        bool sib_fit = false;
         for (int id = 0; id < TDI8_NUM_CONFIGS; ++id)
-            if (taken[id]) list[n3++] = Cand{static_cfg(id), bpc[id]};
+            if (taken[id] && fits(static_cfg(id))) sib_fit = true;
+        for (int id = 0; id < TDI8_NUM_CONFIGS; ++id)
+            if (taken[id] && (!sib_fit || fits(static_cfg(id)))) list[n3++] = Cand{static_cfg(id), bpc[id]};
         if (M <= hw.skinny_max_m) {
             int best_bm = 0;
             for (int id = 0; id < TDI8_NUM_CONFIGS; ++id) {
