@@ -304,6 +304,48 @@ def selector_report(t):
                   f"{times[best]:.2f} | {100.0 * (times[pick] / times[best] - 1):.0f}% | {len(times)} |", flush=True)
             del sets, ref
             torch.cuda.empty_cache()
+    # the implicit-GEMM convolution layers: every general configuration
+    import synthetic
+    print()
+    print("| conv layer | selected | selected µs | fastest | fastest µs | regret | all general configurations (µs) |")
+    print("|---|---|---|---|---|---|---|")
+    for name, ((N, H, W, C, K, R, S), pad, stride) in CONV_WORKLOADS.items():
+        P = t.conv2d_output_extent(H, R, pad[0], stride[0], 1)
+        Q = t.conv2d_output_extent(W, S, pad[1], stride[1], 1)
+        x, w = synthetic.conv_inputs(N, H, W, C, K, R, S, 0)
+        byts = x.size + w.size + 4 * N * P * Q * K
+        nsets = max(2, min(64, -(-3 * MALL_BYTES // byts)))
+        sets = [(torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda(),
+                 torch.empty((N, P, Q, K), dtype=torch.int32, device="cuda")) for _ in range(nsets)]
+        pick = t.conv2d_select_config(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], 1, 1)
+        times, ref = {}, None
+        for c in [table[pick]] + [c for c in table if c.family == 0 and c.id != pick]:
+            args = [(c.id, N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], 1, 1, a.data_ptr(),
+                     b.data_ptr(), y.data_ptr(), sh) for (a, b, y) in sets]
+            t0 = time.perf_counter(); i = 0
+            while time.perf_counter() - t0 < 0.15 or i < nsets:
+                st = t.conv2d_s8s8s32_nhwc_with_config(*args[i % nsets]); i += 1
+                assert st == t.OK, t.tdi8_status_string(st)
+                if i % 64 == 0:
+                    torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for j in range(100):
+                t.conv2d_s8s8s32_nhwc_with_config(*args[j % nsets])
+            e1.record(); torch.cuda.synchronize()
+            times[c.id] = e0.elapsed_time(e1) * 10
+            t.conv2d_s8s8s32_nhwc_with_config(*args[0]); torch.cuda.synchronize()
+            if ref is None:
+                ref = sets[0][2].clone()
+            else:
+                assert torch.equal(sets[0][2], ref), f"config {c.id} differs from config {pick} on {name}"
+        best = min(times, key=times.get)
+        allc = " ".join(f"{k}:{v:.1f}" for k, v in sorted(times.items()))
+        print(f"| {name} | {pick} | {times[pick]:.2f} | {best} | {times[best]:.2f} | "
+              f"{100.0 * (times[pick] / times[best] - 1):.0f}% | {allc} |", flush=True)
+        del sets, ref
+        torch.cuda.empty_cache()
 
 
 def main():
