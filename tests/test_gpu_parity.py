@@ -48,6 +48,52 @@ def test_every_config_small_and_ragged(lib, bcm):
             check_case(DeviceCase(A, B, bcm), f"with_config[{c.id}]", config=c.id)
 
 
+EDGE_MN = [1, 15, 16, 17, 31, 32, 33, 255, 256, 257]
+EDGE_K = [0, 1, 4, 27, 63, 64, 65, 777]
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_edge_grid_sample_every_config(lib, bcm):
+    """Every compiled configuration forced on a seeded sample of the edge
+    grid M, N in EDGE_MN x K in EDGE_K (24 shapes per configuration and
+    layout, different per configuration), with padded leading dimensions on
+    every other shape."""
+    t = lib
+    grid = [(m, n, k) for m in EDGE_MN for n in EDGE_MN for k in EDGE_K]
+    for c in table(t):
+        rng = np.random.default_rng(1000 + c.id + (0 if bcm else 500))
+        for i, gi in enumerate(rng.choice(len(grid), 24, replace=False)):
+            M, N, K = grid[gi]
+            A, B = synthetic.gemm_inputs(M, N, K, seed=int(gi))
+            if i % 2:
+                case = DeviceCase(A, B, bcm, lda=max(K, 1) + 3, ldb=(max(K, 1) if bcm else max(N, 1)) + 5, ldc=N + 2)
+            else:
+                case = DeviceCase(A, B, bcm)
+            if K == 0:
+                check_case(case, f"edge cfg{c.id}", config=c.id, expect=np.zeros((M, N), np.int32))
+            else:
+                check_case(case, f"edge cfg{c.id}", config=c.id)
+
+
+def test_split_k_deterministic(lib):
+    """The K-split form adds partial tiles with atomics in whatever order the
+    blocks finish; integer addition makes the bytes identical every time."""
+    t = lib
+    M, N, K = 256, 256, 32768
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert t.tile_config_split_k(t.select_tile_config(M, N, K), M, N, K, cus) > 1
+    A, B = synthetic.gemm_inputs(M, N, K, seed=21)
+    case = DeviceCase(A, B, True)
+    first = None
+    for _ in range(5):
+        case.c_buf.fill_(-123456789)
+        assert case.run(None) == t.OK
+        C, _ = case.result()
+        first = C if first is None else first
+        assert np.array_equal(C, first)
+    assert np.array_equal(first, case.oracle())
+
+
 @pytest.mark.parametrize("bcm", [True, False])
 def test_split_k_every_general_config(lib, bcm):
     """One tile and a long K: the unpredicated form splits K into slices whose
