@@ -94,6 +94,24 @@ def test_split_k_deterministic(lib):
     assert np.array_equal(first, case.oracle())
 
 
+def test_skinny_row_major_column_groups(lib):
+    """Row-major B on a skinny configuration: when 128-column groups and the
+    K slices (K tile 512 for 16-row tiles, 256 for 32-row ones) divide the
+    problem, a block covers 128 columns over 1/G of K (G = 128 / block width)
+    and adds into a zeroed C; otherwise the per-tile form runs.  Both must
+    equal the oracle, and the ldc padding must survive the zeroing."""
+    t = lib
+    for c in table(t):
+        if c.family != 1:
+            continue
+        G = 128 // c.block_n
+        kt = G * (512 if c.block_m == 16 else 256)
+        for (M, N, K, ldc_pad) in [(c.block_m, 128, kt, 0), (2 * c.block_m, 384, 2 * kt, 8),
+                                   (c.block_m, 256, 3 * kt, 4), (c.block_m, 128, kt + c.block_k, 0)]:
+            A, B = synthetic.gemm_inputs(M, N, K, seed=M + N + K + c.id)
+            check_case(DeviceCase(A, B, False, ldc=N + ldc_pad), f"rr groups cfg{c.id}", config=c.id)
+
+
 @pytest.mark.parametrize("bcm", [True, False])
 def test_split_k_every_general_config(lib, bcm):
     """One tile and a long K: the unpredicated form splits K into slices whose

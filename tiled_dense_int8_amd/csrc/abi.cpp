@@ -126,6 +126,20 @@ DeviceState *current_device(int *status) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Zero the C window, then launch a K-split kernel whose blocks (one per tile
+// and K slice) add their partial sums into it.
+int launch_split(const void *kernel, GemmArgs &g, dim3 grid, dim3 block, hipStream_t stream) {
+    const int64_t quads = static_cast<int64_t>(g.M) * (g.N / 4);
+    const unsigned zb = static_cast<unsigned>(quads / 256 + 1 < 2048 ? quads / 256 + 1 : 2048);
+    void *args[] = {&g};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&zero_c_kernel), dim3(zb), dim3(256), args, 0,
+                                   stream);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipLaunchKernel(kernel, grid, block, args, 0, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return TDI8_OK;
+}
+
 int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
            int32_t *C, int ldc, hipStream_t stream, int num_cu) {
     const StaticCfg c = static_cfg(id);
@@ -155,23 +169,26 @@ int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, cons
         const bool b_ok = aligned(B, 16) && ldb % 16 == 0;
         fast = M % c.bm == 0 && N % c.bn == 0 && K % c.bk == 0 && a_ok && b_ok && c_ok;
         if (fast) g.splits = split_k_for(c, M, N, K, num_cu);
-        if (g.splits > 1) {
-            // zero the C window, then one block per tile and K slice adds into it
-            const int64_t quads = static_cast<int64_t>(M) * (N / 4);
-            const unsigned zb = static_cast<unsigned>(quads / 256 + 1 < 2048 ? quads / 256 + 1 : 2048);
-            void *zargs[] = {&g};
-            hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&zero_c_kernel), dim3(zb), dim3(256),
-                                           zargs, 0, stream);
-            if (e != hipSuccess) return hip_fail(e);
-            grid = dim3(static_cast<unsigned>(tm * tn * g.splits));
-            void *args[] = {&g};
-            e = hipLaunchKernel(kernels()[id].split[bcol ? 1 : 0], grid, block, args, 0, stream);
-            if (e != hipSuccess) return hip_fail(e);
-            return TDI8_OK;
-        }
+        if (g.splits > 1)
+            return launch_split(kernels()[id].split[bcol ? 1 : 0], g, dim3(static_cast<unsigned>(tm * tn * g.splits)),
+                                block, stream);
     } else {
         // the unpredicated forms move B by 16-byte LDS DMA loads in both layouts
         fast = M % c.bm == 0 && N % c.bn == 0 && K % c.bk == 0 && a_ok && aligned(B, 16) && ldb % 16 == 0 && c_ok;
+        // Row-major B: the column-group form (kernel_table.h) when its
+        // 128-column groups and K slices divide the problem.
+        const int groups = kRrGroupCols / c.bn;
+        if (!bcol && fast && N % kRrGroupCols == 0 && K % (groups * rr_group_bk(c.bm)) == 0) {
+            const int64_t tm = M / c.bm;
+            const int64_t tn = N / kRrGroupCols;
+            if (tm * tn * groups <= INT_MAX / 512) {
+                g.tiles_m = static_cast<int>(tm);
+                g.tiles_n = static_cast<int>(tn);
+                g.splits = groups;
+                return launch_split(kernels()[id].rr_group, g, dim3(static_cast<unsigned>(tm * tn * groups)),
+                                    dim3(512), stream);
+            }
+        }
         // the predicated row-major form covers 64 columns per block
         const int bn = (bcol || fast) ? c.bn : 64;
         const int64_t tm = (M + static_cast<int64_t>(c.bm) - 1) / c.bm;

@@ -51,6 +51,23 @@ static const void *conv_entry() {
         return nullptr;
 }
 
+// Row-major B column-group form of the skinny family: 8 waves, one per
+// 16-column slice of the 128-column group; 16 rows (one instruction tile,
+// K tile 512, two stages) or 32 rows (two instruction tiles, K tile 256,
+// three stages).
+template <class P>
+static const void *rr_group_entry() {
+    if constexpr (P::family == 1 && P::mt == 1) {
+        static_assert(rr_group_bk(16) == 512, "K tile of the 16-row form");
+        return reinterpret_cast<const void *>(&gemm_rc_pipelined_kernel<16, 1, 8, 1, 1, 512, 2, true, true>);
+    } else if constexpr (P::family == 1 && P::mt == 2) {
+        static_assert(rr_group_bk(32) == 256, "K tile of the 32-row form");
+        return reinterpret_cast<const void *>(&gemm_rc_pipelined_kernel<16, 1, 8, 2, 1, 256, 3, true, true>);
+    } else {
+        return nullptr;
+    }
+}
+
 void TDI8_CAT(register_cfg_, TDI8_CFG)(KernelSet *ks) {
     using P = CfgParams<TDI8_CFG>;
     ks->kernel[0][0] = entry<P, false, false>();
@@ -60,6 +77,7 @@ void TDI8_CAT(register_cfg_, TDI8_CFG)(KernelSet *ks) {
     ks->split[0] = split_entry<P, false>();
     ks->split[1] = split_entry<P, true>();
     ks->conv = conv_entry<P>();
+    ks->rr_group = rr_group_entry<P>();
 }
 
 }  // namespace tdi8

@@ -25,7 +25,16 @@ struct KernelSet {
     const void *kernel[2][2];
     const void *split[2];
     const void *conv;   // implicit-GEMM convolution form (null for the skinny family)
+    const void *rr_group;  // row-major B column-group form (skinny family only)
 };
+
+// Row-major B column-group form of a skinny configuration (BM x BN tile):
+// one block covers BM x kRrGroupCols outputs over 1/G of K, G = kRrGroupCols
+// / BN, so the grid keeps the configuration's block count while every B row
+// segment a block reads is a whole 128-byte line; the G partial sums of a
+// tile are added into a zeroed C.  K tile of the form per block height:
+constexpr int kRrGroupCols = 128;
+constexpr int rr_group_bk(int bm) { return bm == 16 ? 512 : 256; }
 
 // One registration function per configuration, each defined in its own
 // translation unit so the instantiations compile in parallel.

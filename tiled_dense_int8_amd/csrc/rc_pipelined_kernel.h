@@ -101,7 +101,7 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
     static_assert(STAGES >= 2, "at least two stages");
     static_assert(KS % 2 == 0, "operand double buffer needs an even number of K steps per tile");
     constexpr int CPRB = BN / 16;                // 16-byte chunks per row-major B row
-    static_assert(!BROW || (MF == 32 && CPRB >= 4 && (BK * BN) % 1024 == 0), "row-major B form");
+    static_assert(!BROW || (CPRB >= 4 && (BK * BN) % 1024 == 0), "row-major B form");
     using Acc = typename Mfma<MF>::Acc;
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
 
@@ -238,15 +238,18 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
     // values).  For the 32x32x32 operand, lane l (group q = l / 16, c = l % 16)
     // needs column n = l % 32 and K = 16 (l / 32) .. +15: group q reads
     // columns 16 (q % 2) .. +15 of K rows 16 (q / 2) + (0..7) and then + 8.
+    // For the 16x16x64 operand lane l needs column l % 16 and K = 16 q .. +15.
     int offbt[NT][2];
     if constexpr (BROW) {
         const int q = lane >> 4, c = lane & 15;
+        const int colgrp = MF == 32 ? (q & 1) : 0;
+        const int kgrp = MF == 32 ? (q >> 1) : q;
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            const int nb = wn * (NT * MF) + j * MF + 16 * (q & 1);
+            const int nb = wn * (NT * MF) + j * MF + 16 * colgrp;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const int k = 16 * (q >> 1) + 8 * half + (c >> 1);
+                const int k = 16 * kgrp + 8 * half + (c >> 1);
                 offbt[j][half] = A_BYTES_ + k * BN + 16 * ((nb >> 4) ^ brow_swizzle<BN>(k)) + 8 * (c & 1);
             }
         }
@@ -267,9 +270,10 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
         } else if constexpr (!BROW) {
             fb[buf][r - MT] = *reinterpret_cast<const i32x4 *>(base + offb[r - MT] + 16 * (c ^ swb[r - MT]));
         } else {
-            // K step ks is 32 rows further down; the swizzle repeats every 32 rows
-            const int8_t *p0 = base + offbt[r - MT][0] + ks * MF * BN;
-            const int8_t *p1 = base + offbt[r - MT][1] + ks * MF * BN;
+            // K step ks is KSTEP rows further down; the swizzle's period (8 rows,
+            // 16 for BN = 512) divides KSTEP
+            const int8_t *p0 = base + offbt[r - MT][0] + ks * KSTEP * BN;
+            const int8_t *p1 = base + offbt[r - MT][1] + ks * KSTEP * BN;
             typedef int v2i_t __attribute__((ext_vector_type(2)));
             typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
             const v2i_t lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)(p0));
@@ -402,7 +406,6 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
         // in passes of RP (a multiple of the 32-row instruction tile) that fit
         // the stage buffers with a 16-byte pad per row (the pad keeps the
         // 32 rows written by one instruction on different banks).
-        static_assert(MF == 32, "the split epilogue assumes the 32x32 accumulator layout");
         constexpr int LDS_TOTAL = STAGES * STAGE;
         constexpr int RS = BN + 4;                                  // int32 per LDS row
         constexpr int RP0 = (LDS_TOTAL / (RS * 4)) / MF * MF;
@@ -418,12 +421,16 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     const int cb = wn * (NT * MF) + j * MF;
+                    if constexpr (MF == 32) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int r = rb - p0 + (lane & 31);
-                        const int c = cb + 8 * q + 4 * (lane >> 5);
-                        *reinterpret_cast<i32x4 *>(cl + r * RS + c) =
-                            i32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                        for (int q = 0; q < 4; ++q) {
+                            const int r = rb - p0 + (lane & 31);
+                            const int c = cb + 8 * q + 4 * (lane >> 5);
+                            *reinterpret_cast<i32x4 *>(cl + r * RS + c) =
+                                i32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                        }
+                    } else {
+                        *reinterpret_cast<i32x4 *>(cl + (rb - p0 + (lane & 15)) * RS + cb + 4 * (lane >> 4)) = acc[i][j];
                     }
                 }
             }

@@ -44,7 +44,8 @@ namespace tdi8 {
 // Permutation of the 16-byte chunks of LDS row r (CPR chunks per row).
 template <int CPR>
 __device__ __forceinline__ int chunk_swizzle(int r) {
-    static_assert(CPR == 4 || CPR == 8, "BK must be 64 or 128");
+    static_assert(CPR == 4 || CPR == 8 || CPR == 16 || CPR == 32, "BK must be 64, 128, 256 or 512");
+    if constexpr (CPR >= 16) return r & 15;
     if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
     else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
 }
