@@ -84,7 +84,7 @@ class Cfg:
     block_k: int
     threads: int
     blocks_per_cu: int
-    stages: int = 1   # pipeline depth of the compiled kernel; only tells siblings apart
+    stages: int = 1   # pipeline depth of the compiled kernel; not used by the selection
 
     @property
     def block_m_threads(self) -> int:
@@ -136,7 +136,7 @@ def reuse1_sibling(c: Cfg, table: list[Cfg]) -> Cfg | None:
     for d in table:
         if (d.family == c.family and d.mfma_m == c.mfma_m and d.mfma_n == c.mfma_n
                 and d.waves_m == c.waves_m and d.waves_n == c.waves_n
-                and d.block_k == c.block_k and d.stages == c.stages and d.m_tiles == 1 and d.n_tiles == 1):
+                and d.block_k == c.block_k and d.m_tiles == 1 and d.n_tiles == 1):
             return d
     return None
 

@@ -99,9 +99,9 @@ def test_config_table_shape():
             assert c.lds_bytes <= 160 * 1024
             continue
         sib = tab[c.reuse1_id]
-        assert (sib.family, sib.mfma_m, sib.waves_m, sib.waves_n, sib.waves_k, sib.block_k, sib.stages,
-                sib.m_tiles, sib.n_tiles) == (c.family, c.mfma_m, c.waves_m, c.waves_n, c.waves_k, c.block_k,
-                                              c.stages, 1, 1)
+        # the sibling keeps the thread split and K tile; its pipeline depth may differ
+        assert (sib.family, sib.mfma_m, sib.waves_m, sib.waves_n, sib.waves_k, sib.block_k,
+                sib.m_tiles, sib.n_tiles) == (c.family, c.mfma_m, c.waves_m, c.waves_n, c.waves_k, c.block_k, 1, 1)
         if c.family == 0:
             assert c.lds_bytes == c.stages * (c.block_m + c.block_n) * c.block_k <= 160 * 1024
             assert c.stages >= 2 and (c.block_k // (32 if c.mfma_m == 32 else 64)) % 2 == 0

@@ -34,9 +34,9 @@
     X(4, 0, 32, 2, 2, 1, 2, 1, 64, 4)   /* 128 x  64, 4 waves */     \
     X(5, 0, 32, 2, 2, 1, 1, 1, 64, 4)   /*  64 x  64, reuse 1 */     \
     X(6, 0, 32, 2, 2, 1, 4, 4, 64, 4)   /* 256 x 256, 4 waves */     \
-    X(7, 0, 32, 2, 4, 1, 1, 1, 128, 2)  /*  64 x 128, reuse 1 */     \
+    X(7, 0, 32, 2, 4, 1, 1, 1, 128, 3)  /*  64 x 128, reuse 1 */     \
     X(8, 0, 32, 4, 2, 1, 2, 4, 128, 2)  /* 256 x 256, 8 waves */     \
-    X(9, 0, 32, 4, 2, 1, 1, 1, 128, 2)  /* 128 x  64, reuse 1 */     \
+    X(9, 0, 32, 4, 2, 1, 1, 1, 128, 3)  /* 128 x  64, reuse 1 */     \
     X(10, 0, 32, 2, 2, 1, 4, 4, 128, 2) /* 256 x 256, BK 128 */      \
     X(11, 0, 32, 2, 2, 1, 1, 1, 128, 2) /*  64 x  64, reuse 1 */     \
     X(12, 1, 16, 1, 1, 16, 1, 1, 2048, 1) /* skinny 16 x 16, 16 K-waves */ \

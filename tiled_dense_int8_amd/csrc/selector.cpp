@@ -66,7 +66,7 @@ StaticCfg static_cfg(int id) {
     s.reuse1_id = -1;
     for (const Desc &e : kDesc) {
         if (e.family == d.family && e.mf == d.mf && e.wm == d.wm && e.wn == d.wn && e.wk == d.wk &&
-            e.bk == d.bk && e.st == d.st && e.mt == 1 && e.nt == 1) {
+            e.bk == d.bk && e.mt == 1 && e.nt == 1) {
             s.reuse1_id = e.id;
             break;
         }
