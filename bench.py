@@ -248,6 +248,33 @@ REGRET_SHAPES = [(256, 256, 256), (4096, 4096, 4096), (16, 4096, 4096), (1000, 3
                  (4096, 16, 4096), (333, 777, 999)]
 
 
+PRUNE_THRESHOLD = 0.85
+
+
+def reuse_pruning(times_by_test, table, theta=PRUNE_THRESHOLD):
+    """Claim 3, second alternative: list the data-reuse schemes (family,
+    m_tiles, n_tiles) of the compiled configurations, take a scheme's speed
+    on each test shape as its fastest configuration's time relative to the
+    fastest of all configurations timed there, and exclude the schemes below
+    `theta` on every test shape they were timed on.  The reuse-1 schemes
+    stay whatever they measure: claim 4's fallback reduces every
+    configuration to reuse 1, so it needs them.  Returns rows (scheme,
+    config ids, tests, lowest relative speed, highest, excluded)."""
+    schemes = {}
+    for c in table:
+        schemes.setdefault((c.family, c.m_tiles, c.n_tiles), []).append(c.id)
+    rows = []
+    for key, ids in sorted(schemes.items()):
+        rel = []
+        for times in times_by_test.values():
+            mine = [times[i] for i in ids if i in times]
+            if mine:
+                rel.append(min(times.values()) / min(mine))
+        excluded = bool(rel) and key[1:] != (1, 1) and all(r < theta for r in rel)
+        rows.append((key, ids, len(rel), min(rel) if rel else None, max(rel) if rel else None, excluded))
+    return rows
+
+
 def selector_report(t):
     """Time every applicable compiled configuration on a suite of shapes (both
     B layouts, inputs rotating as in the headline timing), and compare the
@@ -260,6 +287,7 @@ def selector_report(t):
     props = torch.cuda.get_device_properties(0)
     hw = t.HwInfo(props.multi_processor_count, 1024, 256, 32)
     routes = {t.ROUTE_GENERAL: "", t.ROUTE_FALLBACK: " reuse-1", t.ROUTE_SKINNY: " skinny"}
+    times_by_test = {}
     print("| M×N×K | B | selected (route) | selected µs | fastest | fastest µs | regret | configs timed |")
     print("|---|---|---|---|---|---|---|---|")
     for (M, N, K) in REGRET_SHAPES:
@@ -298,12 +326,26 @@ def selector_report(t):
                     ref = sets[0][2].clone()
                 else:
                     assert torch.equal(sets[0][2], ref), f"config {c.id} differs from config {pick} at {M}x{N}x{K}"
+            times_by_test[(M, N, K, bcm)] = times
             best = min(times, key=times.get)
             route = routes.get(sel.route, "")
             print(f"| {M}×{N}×{K} | {'col' if bcm else 'row'} | {pick}{route} | {times[pick]:.2f} | {best} | "
                   f"{times[best]:.2f} | {100.0 * (times[pick] / times[best] - 1):.0f}% | {len(times)} |", flush=True)
             del sets, ref
             torch.cuda.empty_cache()
+    # claim 3's performance test over the same shapes and layouts
+    print()
+    print(f"Claim 3 reuse-scheme test (threshold {PRUNE_THRESHOLD}: a scheme is excluded when its fastest "
+          "configuration is below that fraction of the fastest configuration's speed on every test shape; "
+          "reuse-1 schemes are kept):")
+    print()
+    print("| family | m_tiles × n_tiles | configurations | tests | lowest | highest | measured | compiled in |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (fam, mt, nt), ids, ntest, lo, hi, excl in reuse_pruning(times_by_test, table):
+        compiled = all(table[i].excluded for i in ids)
+        print(f"| {'general' if fam == 0 else 'skinny'} | {mt} × {nt} | {' '.join(map(str, ids))} | {ntest} | "
+              f"{lo:.2f} | {hi:.2f} | {'excluded' if excl else 'kept'} | {'excluded' if compiled else 'kept'} |",
+              flush=True)
     # the implicit-GEMM convolution layers: every general configuration
     import synthetic
     print()

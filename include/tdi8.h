@@ -120,6 +120,9 @@ typedef struct {
     int vgprs, agprs;    /* per lane, from the compiled kernel (0 before a device is seen) */
     int blocks_per_cu;   /* resident blocks per compute unit, from the occupancy query */
     int reuse1_id;       /* configuration with the same thread split and m_tiles = n_tiles = 1 */
+    int excluded;        /* 1: its reuse scheme (family, m_tiles, n_tiles) was excluded by the
+                            performance test of claim 3 (second alternative); the selection drops
+                            it at step 2, gemm_s8s8s32_with_config still runs it */
 } tdi8_tile_config;
 
 /* Number of compiled configurations; ids are 0 .. count-1. */

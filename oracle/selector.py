@@ -32,7 +32,9 @@ Readings:
       extent (16), and the block has at most max_threads_per_block threads.
   claim 3: a configuration survives step 2 if blocks_per_cu * threads, the
       register-limited number of active threads on a compute unit, is at least
-      min_active_threads (one wave per SIMD: 4 * 64 on CDNA4).
+      min_active_threads (one wave per SIMD: 4 * 64 on CDNA4), and if its
+      data-reuse scheme was not excluded by the claim's second alternative, a
+      performance test over many product sizes (an input here: Cfg.excluded).
   claim 4: min_theory_block_num = num_cu * blocks_per_cu and
       Thread_Blocks = ceil(m / BM) * ceil(n / BN).  A configuration survives if
       Thread_Blocks >= min_theory_block_num; if none does, every step-2
@@ -85,6 +87,7 @@ class Cfg:
     threads: int
     blocks_per_cu: int
     stages: int = 1   # pipeline depth of the compiled kernel; not used by the selection
+    excluded: bool = False  # reuse scheme excluded by claim 3's performance test
 
     @property
     def block_m_threads(self) -> int:
@@ -129,7 +132,8 @@ def step2_ok(c: Cfg, hw: Hw) -> bool:
     split_ok = (c.block_m_threads % c.mfma_m == 0 and c.block_n_threads % c.mfma_n == 0
                 and c.block_m_threads >= 16 and c.block_n_threads >= 16
                 and c.threads <= hw.max_threads_per_block)
-    return split_ok and c.blocks_per_cu >= 1 and c.blocks_per_cu * c.threads >= hw.min_active_threads
+    return (not c.excluded and split_ok and c.blocks_per_cu >= 1
+            and c.blocks_per_cu * c.threads >= hw.min_active_threads)
 
 
 def reuse1_sibling(c: Cfg, table: list[Cfg]) -> Cfg | None:

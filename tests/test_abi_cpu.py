@@ -112,7 +112,7 @@ def test_config_table_shape():
 def oracle_table(bpc):
     fam = {0: "general", 1: "skinny"}
     return [Cfg(c.id, fam[c.family], c.mfma_m, c.mfma_n, c.waves_m, c.waves_n, c.m_tiles, c.n_tiles,
-                c.block_k, c.threads, bpc[c.id], c.stages) for c in library_table()]
+                c.block_k, c.threads, bpc[c.id], c.stages, bool(c.excluded)) for c in library_table()]
 
 
 def fake_bpc(lds_per_cu=160 * 1024, waves_per_cu=32):

@@ -248,7 +248,7 @@ def test_selection_on_device_matches_oracle(lib):
     assert all(c.blocks_per_cu >= 1 for c in tab)
     fam = {0: "general", 1: "skinny"}
     otab = [Cfg(c.id, fam[c.family], c.mfma_m, c.mfma_n, c.waves_m, c.waves_n, c.m_tiles, c.n_tiles,
-                c.block_k, c.threads, c.blocks_per_cu, c.stages) for c in tab]
+                c.block_k, c.threads, c.blocks_per_cu, c.stages, bool(c.excluded)) for c in tab]
     hw = Hw(num_cu=props.multi_processor_count, max_threads_per_block=1024, min_active_threads=256,
             skinny_max_m=32)
     for (M, N, K) in [(256, 256, 256), (4096, 4096, 4096), (16, 4096, 4096), (1000, 3000, 777),

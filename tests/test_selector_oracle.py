@@ -135,3 +135,52 @@ def test_split_k_worked_examples():
     assert split_k(sk, 16, 4096, 65536, 256) == 1
     # 120 compute units, 8 tiles: 16 * 8 = 128 > 120 -> 8
     assert split_k(g64x128, 256, 256, 32768, 120) == 8
+
+
+def test_claim3_excluded_reuse_scheme():
+    """Claim 3's second alternative drops a reuse scheme at step 2.  Scheme
+    4 x 4 of the fake table is id0 (256 x 256) and id4 (128 x 128, 16x16
+    tiles).  4096^2 without them: id1 (1024 >= 512 blocks), id2, id3 and id5
+    fill; the largest ratio 128*128/256 = 64 belongs to id1 alone -> id1."""
+    import dataclasses
+    tab = [dataclasses.replace(c, excluded=c.family == "general" and (c.m_tiles, c.n_tiles) == (4, 4))
+           for c in table()]
+    r = select(4096, 4096, 4096, HW, tab)
+    assert r.trace["step2"] == [1, 2, 3, 5] and r.id == 1 and r.route == 0
+    # 256^2 falls back as before: the siblings {2, 5} are reuse 1 and stay -> id2
+    r = select(256, 256, 4096, HW, tab)
+    assert (r.id, r.route) == (2, 1)
+
+
+def test_reuse_scheme_test_rule():
+    """The performance test's rule, on hand-made timings (µs): relative speed
+    = fastest time on the shape / the scheme's fastest time there."""
+    import importlib.util, os
+    spec = importlib.util.spec_from_file_location(
+        "bench_for_test", os.path.join(os.path.dirname(os.path.dirname(__file__)), "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+
+    class C:
+        def __init__(self, id, fam, mt, nt):
+            self.id, self.family, self.m_tiles, self.n_tiles = id, fam, mt, nt
+
+    tab = [C(0, 0, 4, 2), C(1, 0, 4, 4), C(2, 0, 1, 1), C(3, 0, 2, 2), C(4, 0, 4, 4), C(5, 1, 1, 2)]
+    times = {
+        "a": {0: 10.0, 1: 12.5, 2: 20.0, 3: 11.0, 4: 30.0},   # best 10: scheme 4x4 -> 10/12.5 = 0.8
+        "b": {0: 50.0, 1: 80.0, 2: 40.0, 3: 100.0, 4: 70.0},  # best 40: 4x4 -> 40/70 = 0.571, 2x2 -> 0.4
+        "c": {2: 9.0, 5: 10.0},                                # only the 1x1 and skinny 1x2 timed
+    }
+    rows = {r[0]: r for r in bench.reuse_pruning(times, tab, theta=0.85)}
+    # 4x4: 0.8 and 0.571, below 0.85 on both of its tests -> excluded
+    key, ids, ntest, lo, hi, excl = rows[(0, 4, 4)]
+    assert ids == [1, 4] and ntest == 2 and abs(lo - 40 / 70) < 1e-12 and abs(hi - 0.8) < 1e-12 and excl
+    # 2x2: 10/11 = 0.909 on "a" -> kept though 0.4 on "b"
+    assert rows[(0, 2, 2)][5] is False and abs(rows[(0, 2, 2)][4] - 10 / 11) < 1e-12
+    # 1x1: 0.5, 1.0 and 1.0; reuse 1 is kept in any case
+    assert rows[(0, 1, 1)][5] is False
+    # skinny 1x2: 9/10 = 0.9 on its one test -> kept; at threshold 0.95 -> excluded
+    assert rows[(1, 1, 2)][2] == 1 and rows[(1, 1, 2)][5] is False
+    assert {r[0]: r for r in bench.reuse_pruning(times, tab, theta=0.95)}[(1, 1, 2)][5] is True
+    # 4x2: the fastest on "a" -> kept
+    assert rows[(0, 4, 2)][5] is False

@@ -38,7 +38,7 @@ class TileConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "id", "family", "mfma_m", "mfma_n", "mfma_k", "waves_m", "waves_n", "waves_k",
         "m_tiles", "n_tiles", "block_m", "block_n", "block_k", "stages", "threads", "lds_bytes",
-        "vgprs", "agprs", "blocks_per_cu", "reuse1_id")]
+        "vgprs", "agprs", "blocks_per_cu", "reuse1_id", "excluded")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -439,6 +439,7 @@ int tile_config_info(int id, tdi8_tile_config *out) {
     t.threads = c.threads;
     t.lds_bytes = c.lds_bytes;
     t.reuse1_id = c.reuse1_id;
+    t.excluded = c.excluded;
     int dev = -1;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
         int st = TDI8_OK;

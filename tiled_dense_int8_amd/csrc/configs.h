@@ -46,5 +46,13 @@
     X(16, 1, 16, 1, 1, 8, 2, 1, 1024, 2)  /* skinny 32 x 16, 8 K-waves */  \
     X(17, 1, 16, 1, 1, 4, 2, 2, 1024, 2)  /* skinny 32 x 32, 4 K-waves */
 
+// Claim 3, second alternative: the data-reuse schemes (family, m_tiles,
+// n_tiles) that the performance test over a suite of product sizes found
+// below the threshold on every size (the test is part of
+// `bench.py --selector-report`).  Their configurations stay compiled and
+// callable by id, but the selection drops them at step 2.  Reuse-1 schemes
+// are never listed: claim 4's fallback needs them.
+#define TDI8_EXCLUDED_REUSE(X)
+
 #define TDI8_COUNT_ONE(...) +1
 enum { TDI8_NUM_CONFIGS = 0 TDI8_CONFIG_LIST(TDI8_COUNT_ONE) };

@@ -6,7 +6,9 @@
 //          each at least 16, at most max_threads_per_block threads (claim 2,
 //          matrix-unit case); drop configurations whose register-limited
 //          active threads per compute unit, blocks_per_cu * threads, stay
-//          below the threshold (claim 3, first alternative);
+//          below the threshold (claim 3, first alternative) and those whose
+//          reuse scheme the performance test excluded (claim 3, second
+//          alternative: TDI8_EXCLUDED_REUSE in configs.h);
 //  step 3  Thread_Blocks = ceil(M / BM) * ceil(N / BN) must reach
 //          min_theory_block_num = num_cu * blocks_per_cu; if no configuration
 //          does, the size is too small to fill the compute units and every
@@ -63,6 +65,11 @@ StaticCfg static_cfg(int id) {
     s.mfma_k = d.mf == 32 ? 32 : 64;
     s.lds_bytes = d.family == 0 ? d.st * (s.bm + s.bn) * d.bk
                                 : 2 * (s.bm + s.bn) * (d.bk + 16) + d.mt * d.nt * 64 * 16;
+    s.excluded = 0;
+#define TDI8_EXCLUDE(FAM, MT, NT) \
+    if (d.family == (FAM) && d.mt == (MT) && d.nt == (NT)) s.excluded = 1;
+    TDI8_EXCLUDED_REUSE(TDI8_EXCLUDE)
+#undef TDI8_EXCLUDE
     s.reuse1_id = -1;
     for (const Desc &e : kDesc) {
         if (e.family == d.family && e.mf == d.mf && e.wm == d.wm && e.wn == d.wn && e.wk == d.wk &&
@@ -87,7 +94,7 @@ bool passes_step2(const StaticCfg &c, int bpc, const tdi8_hw_info &hw) {
     const bool split = c.block_m_threads % c.mf == 0 && c.block_n_threads % c.mf == 0 &&
                        c.block_m_threads >= 16 && c.block_n_threads >= 16 &&
                        c.threads <= hw.max_threads_per_block;
-    return split && bpc >= 1 && static_cast<int64_t>(bpc) * c.threads >= hw.min_active_threads;
+    return !c.excluded && split && bpc >= 1 && static_cast<int64_t>(bpc) * c.threads >= hw.min_active_threads;
 }
 
 // Sign of ratio(a) - ratio(b) with ratio = BM*BN/(BM+BN).

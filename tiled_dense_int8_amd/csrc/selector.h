@@ -13,6 +13,7 @@ struct StaticCfg {
     int bm, bn;                            // block tile
     int threads, mfma_k, lds_bytes;
     int reuse1_id;                         // same split with m_tiles = n_tiles = 1, or -1
+    int excluded;                          // reuse scheme excluded by claim 3's performance test
 };
 
 StaticCfg static_cfg(int id);
