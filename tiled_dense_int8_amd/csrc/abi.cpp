@@ -256,7 +256,8 @@ int conv_check(const ConvShape &c, const int8_t *x, const int8_t *w, const int32
     g->K = static_cast<int>(rsc);
     g->splits = 1;
     *cv = ConvParams{c.N, c.H, c.W, c.C, c.R, c.S, static_cast<int>(P), static_cast<int>(Q),
-                     c.sh, c.sw, c.ph, c.pw, c.dh, c.dw, static_cast<int>(rsc)};
+                     c.sh, c.sw, c.ph, c.pw, c.dh, c.dw, static_cast<int>(rsc),
+                     make_fast_div(c.C > 0 ? c.C : 1), make_fast_div(c.S)};
     if (M == 0 || c.K == 0) return TDI8_OK;
     if (!y) return TDI8_ERR_NULL_POINTER;
     if (!aligned(y, 4)) return TDI8_ERR_INVALID_VALUE;

@@ -23,12 +23,35 @@ struct GemmArgs {
 
 // Convolution geometry (NHWC image, KRSC filters): image N x H x W x C,
 // filters R x S, output P x Q, stride sh/sw, zero padding ph/pw, dilation
-// dh/dw; rsc = R * S * C, the reduction length.
+// dh/dw; rsc = R * S * C, the reduction length.  c_div and s_div divide
+// reduction positions by C and by S without a division instruction.
+struct FastDiv {
+    unsigned magic;
+    int shift;
+};
 struct ConvParams {
     int N, H, W, C, R, S, P, Q;
     int sh, sw, ph, pw, dh, dw;
     int rsc;
+    FastDiv c_div, s_div;
 };
+
+// Division by a divisor d >= 1 fixed for the whole launch, for 0 <= n < 2^31
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): with l = ceil(log2 d) and
+// magic = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, magic) + n) >> l.
+// The sum stays below 2^32 because mulhi(n, magic) < n < 2^31.
+inline FastDiv make_fast_div(int d) {
+    int l = 0;
+    while ((int64_t{1} << l) < d) ++l;
+    const uint64_t m = ((uint64_t{1} << 32) * ((uint64_t{1} << l) - static_cast<uint64_t>(d))) /
+                           static_cast<uint64_t>(d) + 1;
+    return FastDiv{static_cast<unsigned>(m), l};
+}
+__device__ __forceinline__ int fast_div(int n, FastDiv f) {
+    const unsigned nn = static_cast<unsigned>(n);
+    return static_cast<int>((__umulhi(nn, f.magic) + nn) >> f.shift);
+}
 
 __device__ __forceinline__ int clamp16(int v) { return v < 0 ? 0 : (v > 16 ? 16 : v); }
 __device__ __forceinline__ int clamp4(int v) { return v < 0 ? 0 : (v > 4 ? 4 : v); }

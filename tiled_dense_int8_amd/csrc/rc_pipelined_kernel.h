@@ -194,9 +194,9 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
             const int kpos = kt * BK + 16 * cch[i];
             if (!cok[i] || kpos >= cv.rsc) return zero_chunk;
             if (!is_a) return src[i] + kpos;
-            const int rs = kpos / cv.C;
+            const int rs = fast_div(kpos, cv.c_div);
             const int c0 = kpos - rs * cv.C;
-            const int r = rs / cv.S;
+            const int r = fast_div(rs, cv.s_div);
             const int ss = rs - r * cv.S;
             const int ih = cih[i] + r * cv.dh;
             const int iw = ciw[i] + ss * cv.dw;
