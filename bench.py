@@ -48,6 +48,7 @@ CONV_WORKLOADS = {
     "conv3x3_14": ((32, 14, 14, 256, 256, 3, 3), (1, 1), (1, 1)),
     "conv1x1_28": ((32, 28, 28, 256, 512, 1, 1), (0, 0), (1, 1)),
     "conv3x3_s2": ((32, 56, 56, 128, 128, 3, 3), (1, 1), (2, 2)),
+    "conv3x3_c3": ((32, 112, 112, 3, 64, 3, 3), (1, 1), (1, 1)),  # first layer: byte-gather form
 }
 
 

@@ -187,10 +187,15 @@ int tile_config_split_k(int config_id, int M, int N, int K, int num_cu);
  * K x R x S x C (KRSC), y is N x P x Q x K with P = conv2d_output_extent(H,
  * R, pad_h, stride_h, dil_h) and Q likewise.  The caller owns all three
  * (device memory); the library allocates nothing and keeps no pointer.
- * Requirements: C a multiple of 16, x and w 16-byte aligned, y 4-byte
- * aligned; R, S, stride and dilation >= 1, padding >= 0.  Errors, all found
- * on the host before anything is enqueued: TDI8_ERR_INVALID_VALUE (a size,
- * the channel multiple, an alignment, or N*P*Q or R*S*C above INT_MAX),
+ * Requirements: y 4-byte aligned; R, S, stride and dilation >= 1, padding
+ * >= 0; any channel count C and any alignment of x and w.  With C a multiple
+ * of 16 and x and w 16-byte aligned, every 16-byte chunk of the lowered
+ * matrix is 16 channels of one tap and goes to LDS by DMA; otherwise (the
+ * first layer of a network, C = 3: reduction 27 for 3 x 3 filters) the rows
+ * are gathered byte by byte into registers, a slower form with the same
+ * result.  Errors, all found on the host before anything is enqueued:
+ * TDI8_ERR_INVALID_VALUE (a size, y's alignment, or N*P*Q or R*S*C above
+ * INT_MAX),
  * TDI8_ERR_NULL_POINTER, TDI8_ERR_ALIASING (y overlaps x or w),
  * TDI8_ERR_UNSUPPORTED_DEVICE, TDI8_ERR_HIP.  N*P*Q == 0 or K == 0 enqueues
  * nothing; C == 0 writes zeros.  Asynchronous on `stream`.  The tile

@@ -197,19 +197,20 @@ def test_conv_validation_and_extent():
     assert t.conv2d_output_extent(8, 3, -1, 1, 1) == t.ERR_INVALID_VALUE
     assert t.conv2d_output_extent(8, 3, 1, 0, 1) == t.ERR_INVALID_VALUE
     assert t.conv2d_validate(*good, A16, A16 + (1 << 16), A16 + (1 << 17)) == t.OK
-    bad_channels = (2, 8, 8, 24, 4, 3, 3, 1, 1, 1, 1, 1, 1)
-    assert t.conv2d_validate(*bad_channels, A16, A16 + (1 << 16), A16 + (1 << 17)) == t.ERR_INVALID_VALUE
+    # any channel count and any alignment of x and w (the byte-gather form)
+    odd_channels = (2, 8, 8, 3, 4, 3, 3, 1, 1, 1, 1, 1, 1)
+    assert t.conv2d_validate(*odd_channels, A16 + 1, A16 + (1 << 16) + 3, A16 + (1 << 17)) == t.OK
     for i, v in [(0, -1), (7, -1), (9, 0), (11, 0), (5, 0)]:
         args = list(good)
         args[i] = v
         assert t.conv2d_validate(*args, A16, A16 + (1 << 16), A16 + (1 << 17)) == t.ERR_INVALID_VALUE, (i, v)
     assert t.conv2d_validate(*good, 0, A16, A16 + (1 << 17)) == t.ERR_NULL_POINTER
     assert t.conv2d_validate(*good, A16, A16 + (1 << 16), 0) == t.ERR_NULL_POINTER
-    assert t.conv2d_validate(*good, A16 + 4, A16 + (1 << 16), A16 + (1 << 17)) == t.ERR_INVALID_VALUE
+    assert t.conv2d_validate(*good, A16, A16 + (1 << 16), A16 + (1 << 17) + 2) == t.ERR_INVALID_VALUE
     # y overlapping x: 2*8*8*16 bytes of x at A16, y starts inside it
     assert t.conv2d_validate(*good, A16, A16 + (1 << 16), A16 + 64) == t.ERR_ALIASING
     # empty output: nothing to check beyond the sizes
     assert t.conv2d_validate(0, 8, 8, 16, 4, 3, 3, 1, 1, 1, 1, 1, 1, 0, 0, 0) == t.OK
     # entry points reject before any device work
-    assert t.conv2d_s8s8s32_nhwc(*bad_channels, A16, A16, A16, 0) == t.ERR_INVALID_VALUE
+    assert t.conv2d_s8s8s32_nhwc(*good, A16, A16 + (1 << 16), A16 + (1 << 17) + 2, 0) == t.ERR_INVALID_VALUE
     assert t.conv2d_s8s8s32_nhwc_with_config(99, *good, A16, A16 + (1 << 16), A16 + (1 << 17), 0) == t.ERR_BAD_CONFIG

@@ -85,6 +85,54 @@ def test_selected_config_shapes(t):
     check(t, (4, 1, 1, 16, 8, 3, 3), (1, 1))
 
 
+ODD = [  # channel counts that are not multiples of 16: the byte-gather form
+    ((2, 9, 11, 3, 24, 3, 3), (1, 1), (1, 1), (1, 1)),
+    ((1, 13, 7, 1, 70, 3, 3), (0, 2), (2, 1), (1, 1)),
+    ((3, 8, 8, 24, 17, 1, 1), (0, 0), (1, 1), (1, 1)),
+    ((1, 17, 15, 5, 130, 5, 3), (2, 1), (1, 2), (2, 1)),
+    ((2, 6, 6, 17, 9, 7, 7), (3, 3), (1, 1), (1, 1)),
+    ((1, 12, 12, 8, 33, 3, 3), (1, 1), (3, 3), (2, 2)),
+]
+
+
+@pytest.mark.parametrize("case", ODD)
+def test_every_general_config_odd_channels(t, case):
+    shape, pad, stride, dil = case
+    for cid in range(t.tile_config_count()):
+        if t.tile_config_info(cid).family != 0:
+            continue
+        check(t, shape, pad, stride, dil, config=cid, seed=cid + 100)
+
+
+def test_first_layers(t):
+    """Three input channels: the contest's 3 x 3 x 3 case (reduction 27) and
+    a 7 x 7 stride-2 stem on a 224 x 224 image."""
+    check(t, (2, 32, 32, 3, 64, 3, 3), (1, 1))
+    check(t, (1, 224, 224, 3, 64, 7, 7), (3, 3), (2, 2))
+
+
+def test_misaligned_operands_take_the_gather_form(t):
+    """C a multiple of 16 but x and w off 16-byte alignment: same bytes as the
+    oracle (and as the aligned DMA form)."""
+    import oracle
+    N, H, W, C, K, R, S = 2, 10, 9, 32, 40, 3, 3
+    x, w = synthetic.conv_inputs(N, H, W, C, K, R, S, 7)
+    P = t.conv2d_output_extent(H, R, 1, 1, 1)
+    Q = t.conv2d_output_extent(W, S, 1, 1, 1)
+    xb = torch.zeros(x.size + 64, dtype=torch.int8, device="cuda")
+    wb = torch.zeros(w.size + 64, dtype=torch.int8, device="cuda")
+    xb[1:1 + x.size].copy_(torch.from_numpy(x.reshape(-1)))
+    wb[3:3 + w.size].copy_(torch.from_numpy(w.reshape(-1)))
+    yb = torch.full((N * P * Q * K + TAIL,), SENT, dtype=torch.int32, device="cuda")
+    note(f"[case] conv misaligned x+1 w+3 N={N} H={H} W={W} C={C} K={K}")
+    assert t.conv2d_s8s8s32_nhwc(N, H, W, C, K, R, S, 1, 1, 1, 1, 1, 1, xb.data_ptr() + 1, wb.data_ptr() + 3,
+                                 yb.data_ptr(), 0) == t.OK
+    torch.cuda.synchronize()
+    flat = yb.cpu().numpy()
+    assert np.array_equal(flat[:N * P * Q * K].reshape(N, P, Q, K), oracle.conv2d(x, w, (1, 1), (1, 1), (1, 1)))
+    assert (flat[N * P * Q * K:] == SENT).all()
+
+
 def test_one_by_one_matches_the_gemm_entry(t):
     """A 1x1, stride-1 convolution is the product of the (N H W) x C image
     matrix with the K x C filter matrix (column-major B)."""
@@ -128,6 +176,7 @@ LAYERS = {  # the layer shapes the bench times (see bench.py)
     "conv3x3_14": ((32, 14, 14, 256, 256, 3, 3), (1, 1), (1, 1)),
     "conv1x1_28": ((32, 28, 28, 256, 512, 1, 1), (0, 0), (1, 1)),
     "conv3x3_s2": ((32, 56, 56, 128, 128, 3, 3), (1, 1), (2, 2)),
+    "conv3x3_c3": ((32, 112, 112, 3, 64, 3, 3), (1, 1), (1, 1)),
 }
 
 

@@ -239,7 +239,6 @@ int conv_check(const ConvShape &c, const int8_t *x, const int8_t *w, const int32
     if (c.N < 0 || c.H < 0 || c.W < 0 || c.C < 0 || c.K < 0 || c.R < 1 || c.S < 1 || c.ph < 0 || c.pw < 0 ||
         c.sh < 1 || c.sw < 1 || c.dh < 1 || c.dw < 1)
         return TDI8_ERR_INVALID_VALUE;
-    if (c.C % 16 != 0) return TDI8_ERR_INVALID_VALUE;
     const int64_t P = conv_extent(c.H, c.R, c.ph, c.sh, c.dh);
     const int64_t Q = conv_extent(c.W, c.S, c.pw, c.sw, c.dw);
     const int64_t M = static_cast<int64_t>(c.N) * P * Q;
@@ -263,7 +262,6 @@ int conv_check(const ConvShape &c, const int8_t *x, const int8_t *w, const int32
     if (!aligned(y, 4)) return TDI8_ERR_INVALID_VALUE;
     if (rsc == 0) return TDI8_OK;
     if (!x || !w) return TDI8_ERR_NULL_POINTER;
-    if (!aligned(x, 16) || !aligned(w, 16)) return TDI8_ERR_INVALID_VALUE;
     const uintptr_t y0 = reinterpret_cast<uintptr_t>(y);
     const uintptr_t y1 = y0 + 4 * static_cast<uint64_t>(M) * static_cast<uint64_t>(c.K);
     const uintptr_t x0 = reinterpret_cast<uintptr_t>(x);
@@ -297,9 +295,12 @@ int conv_entry(int cfg, const ConvShape &c, const int8_t *x, const int8_t *w, in
     if (tm * tn > INT_MAX / sc.threads) return TDI8_ERR_INVALID_VALUE;
     g.tiles_m = static_cast<int>(tm);
     g.tiles_n = static_cast<int>(tn);
+    // 16-byte DMA chunks are 16 channels of one tap: C a multiple of 16 and
+    // 16-byte aligned operands; otherwise the byte-gather form.
+    const bool dma = c.C % 16 == 0 && aligned(x, 16) && aligned(w, 16);
     void *args[] = {&g, &cv};
-    hipError_t e = hipLaunchKernel(kernels()[id].conv, dim3(static_cast<unsigned>(tm * tn)), dim3(sc.threads), args,
-                                   0, stream);
+    hipError_t e = hipLaunchKernel(dma ? kernels()[id].conv : kernels()[id].conv_gather,
+                                   dim3(static_cast<unsigned>(tm * tn)), dim3(sc.threads), args, 0, stream);
     if (e != hipSuccess) return hip_fail(e);
     return TDI8_OK;
 }

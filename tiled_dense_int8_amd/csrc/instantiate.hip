@@ -51,6 +51,14 @@ static const void *conv_entry() {
         return nullptr;
 }
 
+template <class P>
+static const void *conv_gather_entry() {
+    if constexpr (P::family == 0)
+        return reinterpret_cast<const void *>(&conv_gather_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk>);
+    else
+        return nullptr;
+}
+
 // Row-major B column-group form of the skinny family: 8 waves, one per
 // 16-column slice of the 128-column group; 16 rows (one instruction tile,
 // K tile 512, two stages) or 32 rows (two instruction tiles, K tile 256,
@@ -77,6 +85,7 @@ void TDI8_CAT(register_cfg_, TDI8_CFG)(KernelSet *ks) {
     ks->split[0] = split_entry<P, false>();
     ks->split[1] = split_entry<P, true>();
     ks->conv = conv_entry<P>();
+    ks->conv_gather = conv_gather_entry<P>();
     ks->rr_group = rr_group_entry<P>();
 }
 

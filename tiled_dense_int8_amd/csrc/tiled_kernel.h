@@ -71,8 +71,42 @@ struct Mfma<16> {
     }
 };
 
-template <int MF, int WM, int WN, int MT, int NT, int BK, bool BCOL, bool FAST>
-__global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(GemmArgs g) {
+// Sixteen consecutive reduction positions kk .. kk+15 of one implicit-GEMM
+// convolution row, gathered byte by byte (any channel count, any alignment):
+// position k is channel c of tap (r, s), k = (r S + s) C + c, read from the
+// image at (ih0 + r dh, iw0 + s dw); outside the image or past R S C it is 0.
+__device__ __forceinline__ i32x4 conv_gather16(const int8_t *img, int ih0, int iw0, int kk, const ConvParams &cv) {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    int rs = fast_div(kk, cv.c_div);
+    int c = kk - rs * cv.C;
+    int r = fast_div(rs, cv.s_div);
+    int s = rs - r * cv.S;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const int ih = ih0 + r * cv.dh;
+        const int iw = iw0 + s * cv.dw;
+        if (kk + t < cv.rsc && static_cast<unsigned>(ih) < static_cast<unsigned>(cv.H) &&
+            static_cast<unsigned>(iw) < static_cast<unsigned>(cv.W)) {
+            const uint32_t b = static_cast<uint8_t>(img[(static_cast<int64_t>(ih) * cv.W + iw) * cv.C + c]);
+            w[t >> 2] |= b << (8 * (t & 3));
+        }
+        if (++c == cv.C) {
+            c = 0;
+            if (++s == cv.S) {
+                s = 0;
+                ++r;
+            }
+        }
+    }
+    return i32x4{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]), static_cast<int>(w[3])};
+}
+
+// SRC 0: the product of the operands described by g.  SRC 1: implicit-GEMM
+// convolution (A rows gathered from the NHWC image by conv_gather16, B the
+// KRSC filters as column-major K x R S C, C the N P Q x K output).
+template <int MF, int WM, int WN, int MT, int NT, int BK, bool BCOL, bool FAST, int SRC>
+__device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &cv) {
+    static_assert(SRC == 0 || (BCOL && !FAST), "the gathered convolution is the predicated column-major form");
     constexpr int NTH = WM * WN * 64;
     constexpr int BM = WM * MF * MT;
     constexpr int BN = WN * MF * NT;
@@ -110,6 +144,25 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(GemmArgs g) {
     i32x4 rb[BCOL ? B_PER : 1];
     uint32_t rw[BCOL ? 1 : RR_PER * 16];
 
+    // Convolution: image base and tap (0, 0) position of each A slot's row
+    // (row past M: a null base, gathered as zeros).
+    [[maybe_unused]] const int8_t *cimg[SRC == 1 ? A_PER : 1];
+    [[maybe_unused]] int cih[SRC == 1 ? A_PER : 1], ciw[SRC == 1 ? A_PER : 1];
+    if constexpr (SRC == 1) {
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) {
+            const int row = m0 + (tid + i * NTH) / CPR;
+            const int pq = cv.P * cv.Q;
+            const int mm = row < g.M ? row : 0;
+            const int img = mm / pq;
+            const int p = (mm - img * pq) / cv.Q;
+            const int q = mm - img * pq - p * cv.Q;
+            cimg[i] = row < g.M ? g.A + static_cast<int64_t>(img) * cv.H * cv.W * cv.C : nullptr;
+            cih[i] = p * cv.sh - cv.ph;
+            ciw[i] = q * cv.sw - cv.pw;
+        }
+    }
+
     // Global -> registers for K tile starting at k0.
     auto fetch = [&](int k0) {
 #pragma unroll
@@ -120,8 +173,12 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(GemmArgs g) {
                 const int c = (q % CPR) ^ chunk_swizzle<CPR>(r);
                 const int row = m0 + r;
                 const int kk = k0 + 16 * c;
-                const int8_t *p = g.A + static_cast<int64_t>(row) * g.lda + kk;
-                ra[i] = FAST ? load16(p) : load16_masked(p, row < g.M ? clamp16(g.K - kk) : 0);
+                if constexpr (SRC == 1) {
+                    ra[i] = cimg[i] ? conv_gather16(cimg[i], cih[i], ciw[i], kk, cv) : i32x4{0, 0, 0, 0};
+                } else {
+                    const int8_t *p = g.A + static_cast<int64_t>(row) * g.lda + kk;
+                    ra[i] = FAST ? load16(p) : load16_masked(p, row < g.M ? clamp16(g.K - kk) : 0);
+                }
             }
         }
         if constexpr (BCOL) {
@@ -262,6 +319,19 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(GemmArgs g) {
             }
         }
     }
+}
+
+template <int MF, int WM, int WN, int MT, int NT, int BK, bool BCOL, bool FAST>
+__global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(GemmArgs g) {
+    tiled_body<MF, WM, WN, MT, NT, BK, BCOL, FAST, 0>(g, ConvParams{});
+}
+
+// Implicit-GEMM convolution for any channel count and alignment: the
+// predicated kernel with A gathered byte by byte (the DMA form needs 16-byte
+// chunks of 16 channels).
+template <int MF, int WM, int WN, int MT, int NT, int BK>
+__global__ void __launch_bounds__(WM * WN * 64) conv_gather_kernel(GemmArgs g, ConvParams cv) {
+    tiled_body<MF, WM, WN, MT, NT, BK, true, false, 1>(g, cv);
 }
 
 }  // namespace tdi8
