@@ -139,4 +139,22 @@ __device__ __forceinline__ void store4(const GemmArgs &g, int m, int n, i32x4 v)
     }
 }
 
+// store4 with the non-temporal hint, for epilogues whose store instructions
+// write whole 128-byte lines of C (the C-through-LDS epilogues): C is not
+// read again by the kernel, and hinted lines do not evict operand lines
+// other blocks still use.  Four columns in range: one hinted 16-byte store
+// (C need only be 4-byte aligned); the ragged edge goes through store4.
+template <bool FAST>
+__device__ __forceinline__ void store4_nt(const GemmArgs &g, int m, int n, i32x4 v) {
+    typedef i32x4 i32x4_a4 __attribute__((aligned(4)));
+    if (!FAST) {
+        if (m >= g.M) return;
+        if (n + 3 >= g.N) {
+            store4<false>(g, m, n, v);
+            return;
+        }
+    }
+    __builtin_nontemporal_store(v, reinterpret_cast<i32x4_a4 *>(g.C + static_cast<int64_t>(m) * g.ldc + n));
+}
+
 }  // namespace tdi8

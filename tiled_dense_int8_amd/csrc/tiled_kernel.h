@@ -297,24 +297,48 @@ __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &
     }
 
     // Epilogue: lane holds D[n][m] = C[m][n] with four consecutive n per
-    // group of four accumulator registers.
+    // group of four accumulator registers.  32x32 tiles go through the LDS
+    // stages (free after the loop's last barrier) in passes of RP rows, so
+    // each store instruction writes whole rows, with the non-temporal hint.
+    if constexpr (MF == 32) {
+        constexpr int RS = BN + 4;  // int32 per LDS row; the pad spreads the 32 rows of a write over the banks
+        constexpr int RP0 = ((2 * STAGE) / (RS * 4)) / MF * MF;
+        constexpr int RP = RP0 < BM ? RP0 : BM;
+        static_assert(RP >= MF, "stage buffers hold at least one instruction tile of rows");
+        int32_t *cl = reinterpret_cast<int32_t *>(lds);
+        for (int p0 = 0; p0 < BM; p0 += RP) {
+            __syncthreads();
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
+            for (int i = 0; i < MT; ++i) {
+                const int rb = wm * (MT * MF) + i * MF;
+                if (rb < p0 || rb >= p0 + RP) continue;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int mb = m0 + wm * (MT * MF) + i * MF;
-            const int nbase = n0 + wn * (NT * MF) + j * MF;
-            if constexpr (MF == 32) {
-                const int m = mb + (lane & 31);
+                for (int j = 0; j < NT; ++j) {
+                    const int cb = wn * (NT * MF) + j * MF;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = nbase + 8 * q + 4 * (lane >> 5);
-                    i32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    store4<FAST>(g, m, n, v);
+                    for (int q = 0; q < 4; ++q) {
+                        const int r = rb - p0 + (lane & 31);
+                        const int c = cb + 8 * q + 4 * (lane >> 5);
+                        *reinterpret_cast<i32x4 *>(cl + r * RS + c) =
+                            i32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    }
                 }
-            } else {
-                const int m = mb + (lane & 15);
-                const int n = nbase + 4 * (lane >> 4);
+            }
+            __syncthreads();
+            const int rows = BM - p0 < RP ? BM - p0 : RP;
+            for (int idx = tid; idx < rows * (BN / 4); idx += NTH) {
+                const int r = idx / (BN / 4);
+                const int c4 = idx - r * (BN / 4);
+                store4_nt<FAST>(g, m0 + p0 + r, n0 + 4 * c4, *reinterpret_cast<const i32x4 *>(cl + r * RS + 4 * c4));
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int m = m0 + wm * (MT * MF) + i * MF + (lane & 15);
+                const int n = n0 + wn * (NT * MF) + j * MF + 4 * (lane >> 4);
                 store4<FAST>(g, m, n, acc[i][j]);
             }
         }
