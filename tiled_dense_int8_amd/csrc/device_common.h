@@ -139,6 +139,11 @@ __device__ __forceinline__ void store4(const GemmArgs &g, int m, int n, i32x4 v)
     }
 }
 
+// Cache-policy operand of the LDS DMA load: the non-temporal hint, for a
+// stream read once (B when a single block row covers M), so that it does not
+// evict the lines the kernel reads again (A).
+constexpr int kLoadStream = 2;
+
 // store4 with the non-temporal hint, for epilogues whose store instructions
 // write whole 128-byte lines of C (the C-through-LDS epilogues): C is not
 // read again by the kernel, and hinted lines do not evict operand lines

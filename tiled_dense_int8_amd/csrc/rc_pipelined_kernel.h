@@ -206,9 +206,17 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
             return src[i] + (static_cast<int64_t>(ih) * cv.W + iw) * cv.C + c0;
         }
     };
+    // One block row over M: each B byte is read by one block only, so B
+    // streams past the cache and leaves it to A (row-major skinny column
+    // groups, the 16x16x64 split forms: 4-5%).  Compiled into those forms
+    // only: the run-time test cost the 256 x 256 kernel 1%.
+    const bool b_once = SRC == 0 && SPLIT && MF == 16 && g.tiles_m == 1;
     auto issue_one = [&](int kt, int i) {
         int8_t *dst = lds + (kt % STAGES) * STAGE + (i * NW + wave) * 1024;
-        __builtin_amdgcn_global_load_lds(source(i, kt), (lds_void_t *)dst, 16, 0, 0);
+        if (b_once && (i * NW + wave) * 64 >= A_CHUNKS)
+            __builtin_amdgcn_global_load_lds(source(i, kt), (lds_void_t *)dst, 16, 0, kLoadStream);
+        else
+            __builtin_amdgcn_global_load_lds(source(i, kt), (lds_void_t *)dst, 16, 0, 0);
     };
     auto issue = [&](int kt) {
 #pragma unroll
