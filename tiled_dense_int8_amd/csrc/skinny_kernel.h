@@ -163,7 +163,9 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
 
 #if defined(__HIP_DEVICE_COMPILE__)
     __shared__ __attribute__((aligned(1024))) int8_t buf[2][ROWS * RS];
-    __shared__ int32_t red[TILES][64][4];   // block sum, accumulated with LDS atomics
+    // Block sum, accumulated with LDS atomics; element e of lane l at
+    // [tile][e][l], so the 64 lanes of one atomic hit 64 different banks.
+    __shared__ int32_t red[TILES][4][64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -246,12 +248,12 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) atomicAdd(&red[i * NT + j][lane][e], acc[i][j][e]);
+            for (int e = 0; e < 4; ++e) atomicAdd(&red[i * NT + j][e][lane], acc[i][j][e]);
     __syncthreads();
     for (int t = tid; t < TILES * 64; t += WK * 64) {
         const int tile = t >> 6;
         const int l = t & 63;
-        const i32x4 sum = {red[tile][l][0], red[tile][l][1], red[tile][l][2], red[tile][l][3]};
+        const i32x4 sum = {red[tile][0][l], red[tile][1][l], red[tile][2][l], red[tile][3][l]};
         const int m = m0 + 16 * (tile / NT) + (l & 15);
         const int n = n0 + 16 * (tile % NT) + 4 * (l >> 4);
         store4<true>(g, m, n, sum);
@@ -295,7 +297,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
 
 #if defined(__HIP_DEVICE_COMPILE__)
     __shared__ __attribute__((aligned(1024))) int8_t buf[2][STAGE];
-    __shared__ int32_t red[TILES][64][4];
+    __shared__ int32_t red[TILES][4][64];   // as in gemm_skinny_lds_kernel
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -395,12 +397,12 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) atomicAdd(&red[i * NT + j][lane][e], acc[i][j][e]);
+            for (int e = 0; e < 4; ++e) atomicAdd(&red[i * NT + j][e][lane], acc[i][j][e]);
     __syncthreads();
     for (int t = tid; t < TILES * 64; t += WK * 64) {
         const int tile = t >> 6;
         const int l = t & 63;
-        const i32x4 sum = {red[tile][l][0], red[tile][l][1], red[tile][l][2], red[tile][l][3]};
+        const i32x4 sum = {red[tile][0][l], red[tile][1][l], red[tile][2][l], red[tile][3][l]};
         const int m = m0 + 16 * (tile / NT) + (l & 15);
         const int n = n0 + 16 * (tile % NT) + 4 * (l >> 4);
         store4<true>(g, m, n, sum);
