@@ -239,6 +239,48 @@ def test_non_default_stream(lib):
     assert np.array_equal(C, case.oracle()) and (rest == -123456789).all()
 
 
+def test_graph_capture_and_replay(lib):
+    """The entry points only enqueue kernels (no allocation, no memset), so a
+    call can be captured into a HIP graph.  Every replay, with eager work and
+    synchronisations in between, must reproduce the eager bytes: the plain
+    form, the K split (zero-fill kernel then split kernel) and the row-major
+    skinny column groups (also zero fill then split)."""
+    t = lib
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for (M, N, K, bcm) in [(512, 512, 1024, True), (256, 256, 32768, True), (16, 4096, 4096, False)]:
+        note(f"[case] graph capture {M}x{N}x{K} bcm={bcm} config={t.select_tile_config(M, N, K)} "
+             f"splits={t.tile_config_split_k(t.select_tile_config(M, N, K), M, N, K, cus)}")
+        A, B = synthetic.gemm_inputs(M, N, K, seed=5)
+        Ad = torch.from_numpy(A).cuda()
+        Bd = torch.from_numpy(synthetic.store_b(B, bcm)).cuda()
+        want = t.gemm(Ad, Bd, bcm)
+        torch.cuda.synchronize()
+        assert np.array_equal(want.cpu().numpy(), oracle_gemm(A, B))
+        out = torch.empty((M, N), dtype=torch.int32, device="cuda")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            t.gemm(Ad, Bd, bcm, out=out)          # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            t.gemm(Ad, Bd, bcm, out=out)
+        for r in range(4):
+            out.fill_(-7)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, want), f"replay {r}"
+            t.gemm(Ad, Bd, bcm)                   # eager work between replays
+            torch.cuda.synchronize()
+
+
+def oracle_gemm(A, B):
+    import oracle
+    return oracle.gemm(A, B, False)
+
+
 def test_selection_on_device_matches_oracle(lib):
     from oracle.selector import Cfg, Hw, select
     t = lib
