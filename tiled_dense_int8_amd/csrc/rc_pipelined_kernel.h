@@ -68,16 +68,6 @@ __device__ __forceinline__ void tile_of_block(const GemmArgs &g, int bid, int &t
     tn = within / rows;
 }
 
-// Permutation of the 16-byte chunks of a row-major B row k in LDS (BN bytes
-// per row): even values only, varying with k so that the eight rows read by
-// one 16-lane group of a transpose read land on distinct bank groups.
-template <int BN>
-__device__ __forceinline__ int brow_swizzle(int k) {
-    constexpr int CPRB = BN / 16;
-    constexpr int P = BN >= 256 ? 1 : 256 / BN;  // rows sharing one 256-byte bank window
-    return 2 * ((k / P) % (CPRB / 2));
-}
-
 // SPLIT: the grid holds g.splits blocks per tile, slice s of a tile covering
 // K range [s K / splits, (s + 1) K / splits) and adding its partial sums into
 // C (zeroed beforehand) with integer atomics: exact in any order.
@@ -240,26 +230,15 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
         swb[j] = chunk_swizzle<CPR>(r - BM);
     }
 
-    // Row-major B operands come from two transpose reads per fragment.  In
-    // each 16-lane group, lanes 2r and 2r+1 address the two 8-byte halves of
-    // row r of an 8 x 16-byte block and lane c receives column c (eight K
-    // values).  For the 32x32x32 operand, lane l (group q = l / 16, c = l % 16)
-    // needs column n = l % 32 and K = 16 (l / 32) .. +15: group q reads
-    // columns 16 (q % 2) .. +15 of K rows 16 (q / 2) + (0..7) and then + 8.
-    // For the 16x16x64 operand lane l needs column l % 16 and K = 16 q .. +15.
+    // Row-major B operands come from two transpose reads per fragment
+    // (brow_frag_offsets).
     int offbt[NT][2];
     if constexpr (BROW) {
-        const int q = lane >> 4, c = lane & 15;
-        const int colgrp = MF == 32 ? (q & 1) : 0;
-        const int kgrp = MF == 32 ? (q >> 1) : q;
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            const int nb = wn * (NT * MF) + j * MF + 16 * colgrp;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int k = 16 * kgrp + 8 * half + (c >> 1);
-                offbt[j][half] = A_BYTES_ + k * BN + 16 * ((nb >> 4) ^ brow_swizzle<BN>(k)) + 8 * (c & 1);
-            }
+            brow_frag_offsets<MF, BN>(lane, wn * (NT * MF) + j * MF, offbt[j][0], offbt[j][1]);
+            offbt[j][0] += A_BYTES_;
+            offbt[j][1] += A_BYTES_;
         }
     }
 
@@ -278,15 +257,8 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
         } else if constexpr (!BROW) {
             fb[buf][r - MT] = *reinterpret_cast<const i32x4 *>(base + offb[r - MT] + 16 * (c ^ swb[r - MT]));
         } else {
-            // K step ks is KSTEP rows further down; the swizzle's period (8 rows,
-            // 16 for BN = 512) divides KSTEP
-            const int8_t *p0 = base + offbt[r - MT][0] + ks * KSTEP * BN;
-            const int8_t *p1 = base + offbt[r - MT][1] + ks * KSTEP * BN;
-            typedef int v2i_t __attribute__((ext_vector_type(2)));
-            typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
-            const v2i_t lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)(p0));
-            const v2i_t hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)(p1));
-            fb[buf][r - MT] = i32x4{lo[0], lo[1], hi[0], hi[1]};
+            fb[buf][r - MT] = read_tr_frag(base + offbt[r - MT][0] + ks * KSTEP * BN,
+                                           base + offbt[r - MT][1] + ks * KSTEP * BN);
         }
     };
     auto read_frags = [&](int kt, int ks, int buf) {

@@ -50,6 +50,49 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
     else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
 }
 
+// Permutation of the 16-byte chunks of a row-major B row k in LDS (BN bytes
+// per row): even values only, varying with k so that the eight rows read by
+// one 16-lane group of a transpose read land on distinct bank groups.
+template <int BN>
+__device__ __forceinline__ int brow_swizzle(int k) {
+    constexpr int CPRB = BN / 16;
+    constexpr int P = BN >= 256 ? 1 : 256 / BN;  // rows sharing one 256-byte bank window
+    return 2 * ((k / P) % (CPRB / 2));
+}
+
+// Row-major B tile [BK][BN] in LDS (chunks permuted by brow_swizzle): byte
+// offsets, within the B region and for K step 0, of the two transpose reads
+// (ds_read_b64_tr_b8) that gather lane `lane`'s K-major operand for the
+// instruction tile whose columns start at ncol.  In each 16-lane group,
+// lanes 2r and 2r+1 address the two 8-byte halves of row r of an 8 x 16-byte
+// block and lane c receives column c (eight K values).  For the 32x32x32
+// operand, lane l (group q = l / 16, c = l % 16) needs column ncol + l % 32
+// and K = 16 (l / 32) .. +15: group q reads columns 16 (q % 2) .. +15 of K
+// rows 16 (q / 2) + (0..7) and then + 8.  For the 16x16x64 operand lane l
+// needs column ncol + l % 16 and K = 16 q .. +15.  K step ks lies
+// ks * KSTEP * BN bytes further on; the swizzle's period (8 rows, 16 for
+// BN = 512) divides KSTEP.
+template <int MF, int BN>
+__device__ __forceinline__ void brow_frag_offsets(int lane, int ncol, int &lo, int &hi) {
+    const int q = lane >> 4, c = lane & 15;
+    const int colgrp = MF == 32 ? (q & 1) : 0;
+    const int kgrp = MF == 32 ? (q >> 1) : q;
+    const int nb = ncol + 16 * colgrp;
+    const int k0 = 16 * kgrp + (c >> 1);
+    const int k1 = k0 + 8;
+    lo = k0 * BN + 16 * ((nb >> 4) ^ brow_swizzle<BN>(k0)) + 8 * (c & 1);
+    hi = k1 * BN + 16 * ((nb >> 4) ^ brow_swizzle<BN>(k1)) + 8 * (c & 1);
+}
+
+// The two halves of a transposed operand fragment, read at p0 and p1 (LDS).
+__device__ __forceinline__ i32x4 read_tr_frag(const int8_t *p0, const int8_t *p1) {
+    typedef int v2i_t __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
+    const v2i_t lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)(p0));
+    const v2i_t hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)(p1));
+    return i32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 template <int MF>
 struct Mfma;
 
@@ -117,8 +160,8 @@ __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &
     constexpr int B_CHUNKS = BN * CPR;
     constexpr int A_PER = (A_CHUNKS + NTH - 1) / NTH;
     constexpr int B_PER = (B_CHUNKS + NTH - 1) / NTH;
-    constexpr int RR_BLOCKS = (BK / 16) * (BN / 4);    // 16x4 byte blocks of row-major B
-    constexpr int RR_PER = (RR_BLOCKS + NTH - 1) / NTH;
+    constexpr int CPRB = BN / 16;                 // 16-byte chunks per row-major B row
+    static_assert(BCOL || CPRB >= 4, "row-major B tile at least 64 columns wide");
     constexpr int KSTEPS = BK / Mfma<MF>::KSTEP;
     using Acc = typename Mfma<MF>::Acc;
 
@@ -141,8 +184,7 @@ __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &
         for (int j = 0; j < NT; ++j) acc[i][j] = Acc{};
 
     i32x4 ra[A_PER];
-    i32x4 rb[BCOL ? B_PER : 1];
-    uint32_t rw[BCOL ? 1 : RR_PER * 16];
+    i32x4 rb[B_PER];
 
     // Convolution: image base and tap (0, 0) position of each A slot's row
     // (row past M: a null base, gathered as zeros).
@@ -195,20 +237,18 @@ __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &
                 }
             }
         } else {
+            // Row-major B: slot q of the tile holds row k = q / CPRB, source
+            // chunk (q % CPRB) ^ brow_swizzle(k), i.e. 16 consecutive columns.
 #pragma unroll
-            for (int i = 0; i < RR_PER; ++i) {
-                const int u = tid + i * NTH;
-                if (RR_BLOCKS % NTH == 0 || u < RR_BLOCKS) {
-                    const int nb = u % (BN / 4);
-                    const int kq = u / (BN / 4);
-                    const int col = n0 + 4 * nb;
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) {
-                        const int k = k0 + 16 * kq + t;
-                        const int8_t *p = g.B + static_cast<int64_t>(k) * g.ldb + col;
-                        rw[i * 16 + t] = FAST ? *reinterpret_cast<const uint32_t *>(p)
-                                              : load4_masked(p, k < g.K ? clamp4(g.N - col) : 0);
-                    }
+            for (int i = 0; i < B_PER; ++i) {
+                const int q = tid + i * NTH;
+                if (B_CHUNKS % NTH == 0 || q < B_CHUNKS) {
+                    const int k = q / CPRB;
+                    const int c = (q % CPRB) ^ brow_swizzle<BN>(k);
+                    const int kk = k0 + k;
+                    const int col = n0 + 16 * c;
+                    const int8_t *p = g.B + static_cast<int64_t>(kk) * g.ldb + col;
+                    rb[i] = FAST ? load16(p) : load16_masked(p, kk < g.K ? clamp16(g.N - col) : 0);
                 }
             }
         }
@@ -223,38 +263,20 @@ __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &
             if (A_CHUNKS % NTH == 0 || q < A_CHUNKS)
                 *reinterpret_cast<i32x4 *>(base + 16 * q) = ra[i];
         }
-        if constexpr (BCOL) {
 #pragma unroll
-            for (int i = 0; i < B_PER; ++i) {
-                const int q = tid + i * NTH;
-                if (B_CHUNKS % NTH == 0 || q < B_CHUNKS)
-                    *reinterpret_cast<i32x4 *>(base + A_BYTES + 16 * q) = rb[i];
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < RR_PER; ++i) {
-                const int u = tid + i * NTH;
-                if (RR_BLOCKS % NTH == 0 || u < RR_BLOCKS) {
-                    const int nb = u % (BN / 4);
-                    const int kq = u / (BN / 4);
-                    uint32_t t4[4][4];  // [k quad][column]
-#pragma unroll
-                    for (int qd = 0; qd < 4; ++qd) transpose4x4(&rw[i * 16 + 4 * qd], t4[qd]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int r = 4 * nb + j;
-                        const int c = kq ^ chunk_swizzle<CPR>(r);
-                        i32x4 v;
-                        v[0] = static_cast<int32_t>(t4[0][j]);
-                        v[1] = static_cast<int32_t>(t4[1][j]);
-                        v[2] = static_cast<int32_t>(t4[2][j]);
-                        v[3] = static_cast<int32_t>(t4[3][j]);
-                        *reinterpret_cast<i32x4 *>(base + A_BYTES + r * BK + 16 * c) = v;
-                    }
-                }
-            }
+        for (int i = 0; i < B_PER; ++i) {
+            const int q = tid + i * NTH;
+            if (B_CHUNKS % NTH == 0 || q < B_CHUNKS)
+                *reinterpret_cast<i32x4 *>(base + A_BYTES + 16 * q) = rb[i];
         }
     };
+
+    // Row-major B: LDS offsets of this lane's transpose reads (K step 0).
+    [[maybe_unused]] int offbt[BCOL ? 1 : NT][2];
+    if constexpr (!BCOL) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) brow_frag_offsets<MF, BN>(lane, wn * (NT * MF) + j * MF, offbt[j][0], offbt[j][1]);
+    }
 
     // Matrix-core work on LDS stage s.
     auto compute = [&](int s) {
@@ -273,8 +295,13 @@ __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &
             }
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-                const int r = wn * (NT * MF) + j * MF + lrow;
-                xb[j] = *reinterpret_cast<const i32x4 *>(Bs + r * BK + 16 * (c ^ chunk_swizzle<CPR>(r)));
+                if constexpr (BCOL) {
+                    const int r = wn * (NT * MF) + j * MF + lrow;
+                    xb[j] = *reinterpret_cast<const i32x4 *>(Bs + r * BK + 16 * (c ^ chunk_swizzle<CPR>(r)));
+                } else {
+                    constexpr int KSTEP = Mfma<MF>::KSTEP;
+                    xb[j] = read_tr_frag(Bs + offbt[j][0] + ks * KSTEP * BN, Bs + offbt[j][1] + ks * KSTEP * BN);
+                }
             }
 #pragma unroll
             for (int i = 0; i < MT; ++i)
