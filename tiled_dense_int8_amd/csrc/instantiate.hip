@@ -16,11 +16,21 @@
 
 namespace tdi8 {
 
+// Pipeline depth of the unpredicated kernel per B layout.  A configuration's
+// stage count is its column-major kernel's; with row-major B the 64 x 128
+// and 128 x 64 tiles keep two stages, since there three resident blocks per
+// compute unit (instead of two) gain more than the deeper prefetch
+// (512x4096x4096: 29.7 against 31.5 us; 1024x1024x8192: 41.8 against 46.1).
+template <class P, bool BCOL>
+constexpr int stages_for() {
+    return BCOL || P::st < 3 ? P::st : 2;
+}
+
 template <class P, bool BCOL, bool FAST>
 static const void *entry() {
     if constexpr (P::family == 0 && FAST)
         return reinterpret_cast<const void *>(
-            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, P::st, !BCOL, false>);
+            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, stages_for<P, BCOL>(), !BCOL, false>);
     else if constexpr (P::family == 0)
         return reinterpret_cast<const void *>(
             &gemm_tiled_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, BCOL, FAST>);
@@ -38,7 +48,7 @@ template <class P, bool BCOL>
 static const void *split_entry() {
     if constexpr (P::family == 0)
         return reinterpret_cast<const void *>(
-            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, P::st, !BCOL, true>);
+            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, stages_for<P, BCOL>(), !BCOL, true>);
     else
         return nullptr;
 }

@@ -68,6 +68,17 @@ __device__ __forceinline__ void tile_of_block(const GemmArgs &g, int bid, int &t
     tn = within / rows;
 }
 
+// K steps handled as one group by the pipelined schedule: operand reads go out
+// one group ahead and are waited for once per group, so a wave with few
+// matrix instructions per K step (small tiles: f of them) still has about
+// four in flight while its next reads land.  Groups per K tile stay even
+// (the operand double buffer alternates by group).
+constexpr int step_group(int ks, int f) {
+    int g = 1;
+    while (ks % (4 * g) == 0 && 2 * g * f <= 4) g *= 2;
+    return g;
+}
+
 // SPLIT: the grid holds g.splits blocks per tile, slice s of a tile covering
 // K range [s K / splits, (s + 1) K / splits) and adding its partial sums into
 // C (zeroed beforehand) with integer atomics: exact in any order.
@@ -90,6 +101,13 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
     static_assert(A_CHUNKS % 64 == 0, "A region must be whole wave instructions");
     static_assert(STAGES >= 2, "at least two stages");
     static_assert(KS % 2 == 0, "operand double buffer needs an even number of K steps per tile");
+#ifdef TDI8_EXP_NO_GROUP
+    constexpr int G = 1;
+#else
+    constexpr int G = step_group(KS, MT * NT);   // K steps per operand group
+#endif
+    constexpr int KG = KS / G;                   // groups per K tile
+    static_assert(KG % 2 == 0, "operand double buffer needs an even number of groups per tile");
     constexpr int CPRB = BN / 16;                // 16-byte chunks per row-major B row
     static_assert(!BROW || (CPRB >= 4 && (BK * BN) % 1024 == 0), "row-major B form");
     using Acc = typename Mfma<MF>::Acc;
@@ -248,45 +266,51 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = Acc{};
 
-    i32x4 fa[2][MT], fb[2][NT];
-    auto read_one = [&](int kt, int ks, int buf, int r) {
+    // Operand registers: [buffer][K step of the group][fragment].
+    i32x4 fa[2][G][MT], fb[2][G][NT];
+    constexpr int F1 = MT * NT;  // matrix-core instructions per K step
+    constexpr int R1 = MT + NT;  // operand reads per K step
+    // Read rr of group gi of tile kt (K step gi * G + rr / R1, fragment rr % R1).
+    auto read_one = [&](int kt, int gi, int buf, int rr) {
+        const int s = rr / R1, r = rr % R1;
+        const int ks = gi * G + s;
         const int8_t *base = lds + (kt % STAGES) * STAGE;
         const int c = ks * KC + lgrp;
         if (r < MT) {
-            fa[buf][r] = *reinterpret_cast<const i32x4 *>(base + offa[r] + 16 * (c ^ swa[r]));
+            fa[buf][s][r] = *reinterpret_cast<const i32x4 *>(base + offa[r] + 16 * (c ^ swa[r]));
         } else if constexpr (!BROW) {
-            fb[buf][r - MT] = *reinterpret_cast<const i32x4 *>(base + offb[r - MT] + 16 * (c ^ swb[r - MT]));
+            fb[buf][s][r - MT] = *reinterpret_cast<const i32x4 *>(base + offb[r - MT] + 16 * (c ^ swb[r - MT]));
         } else {
-            fb[buf][r - MT] = read_tr_frag(base + offbt[r - MT][0] + ks * KSTEP * BN,
-                                           base + offbt[r - MT][1] + ks * KSTEP * BN);
+            fb[buf][s][r - MT] = read_tr_frag(base + offbt[r - MT][0] + ks * KSTEP * BN,
+                                              base + offbt[r - MT][1] + ks * KSTEP * BN);
         }
     };
-    auto read_frags = [&](int kt, int ks, int buf) {
+    constexpr int F = G * F1;    // matrix-core instructions per group
+    constexpr int R = G * R1;    // operand reads per group
+    auto read_frags = [&](int kt, int gi, int buf) {
 #pragma unroll
-        for (int r = 0; r < MT + NT; ++r) read_one(kt, ks, buf, r);
+        for (int rr = 0; rr < R; ++rr) read_one(kt, gi, buf, rr);
     };
-    constexpr int F = MT * NT;   // matrix-core instructions per K step
-    constexpr int R = MT + NT;   // operand reads per K step
     auto mma_one = [&](int buf, int x) {
-        const int i = x / NT, j = x % NT;
-        acc[i][j] = Mfma<MF>::run(fb[buf][j], fa[buf][i], acc[i][j]);
+        const int s = x / F1, i = (x % F1) / NT, j = x % NT;
+        acc[i][j] = Mfma<MF>::run(fb[buf][s][j], fa[buf][s][i], acc[i][j]);
     };
-    // Read r of a K step is issued after matrix instruction r / 2: two per
-    // instruction, at the front of the step, so the last one has most of the
-    // step to land before the step's closing wait.
+    // Read r of a group is issued after matrix instruction r / 2: two per
+    // instruction, at the front of the group, so the last one has most of the
+    // group to land before the group's closing wait.
     auto read_slot = [](int r) constexpr -> int { return r / 2 < F ? r / 2 : F - 1; };
 
     // One K tile, as a fixed instruction order (each matrix-core instruction
     // followed by the memory operations slotted after it, fenced so the
     // compiler keeps the order):
-    //  * K steps 0 .. KS-2: matrix work of the step, with the operand reads
-    //    of the next step slotted in (read_slot);
-    //  * last step: its operands are already in registers, so first publish
+    //  * groups 0 .. KG-2: matrix work of the group, with the operand reads
+    //    of the next group slotted in (read_slot);
+    //  * last group: its operands are already in registers, so first publish
     //    tile t+1 (own DMA loads of t+1 retired, then a barrier: every wave
     //    is done with buffer t % STAGES), refill that buffer with tile
-    //    t+STAGES, then the step's matrix work with tile t+1's first-step
+    //    t+STAGES, then the group's matrix work with tile t+1's first-group
     //    operands read in between.
-    // Every step ends by retiring its operand reads, so the next step's
+    // Every group ends by retiring its operand reads, so the next group's
     // matrix work starts with its operands in registers.  Issuing a refill
     // right after the barrier that frees its buffer gives it the longest
     // possible time in flight (a whole K tile with two stages).
@@ -299,15 +323,15 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
         constexpr bool NEXT = decltype(next_tag)::value;
         constexpr bool WAITN = decltype(waitn_tag)::value;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int cur = ks & 1;
-            if (ks + 1 < KS) {
+        for (int gi = 0; gi < KG; ++gi) {
+            const int cur = gi & 1;
+            if (gi + 1 < KG) {
 #pragma unroll
                 for (int x = 0; x < F; ++x) {
                     mma_one(cur, x);
 #pragma unroll
                     for (int r = 0; r < R; ++r)
-                        if (read_slot(r) == x) read_one(t, ks + 1, cur ^ 1, r);
+                        if (read_slot(r) == x) read_one(t, gi + 1, cur ^ 1, r);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
