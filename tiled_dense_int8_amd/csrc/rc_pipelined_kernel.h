@@ -14,9 +14,12 @@
 //    tile and frees the buffer just consumed, which is refilled at once with
 //    the tile STAGES ahead (prefetch = double buffering generalised;
 //    "CUDA编程实践" section 3, the data-prefetch paragraph);
-//  * instruction operands are prefetched one K step ahead in registers; the
-//    first step of the next K tile is read right after the barrier, under
-//    the last step's matrix-core work;
+//  * instruction operands are prefetched one group of K steps ahead in
+//    registers (step_group: about four matrix instructions per group); the
+//    first group of the next K tile is read right after the barrier, under
+//    the last group's matrix-core work;
+//  * C leaves through LDS in row passes, every store instruction writing
+//    whole 128-byte lines with the non-temporal hint (store4_nt);
 //  * blocks are ordered so that the blocks resident on one XCD (workgroups
 //    are dealt to the 8 XCDs round-robin) cover a compact group of tiles
 //    and share A and B rows in that XCD's L2 (the contest write-up's

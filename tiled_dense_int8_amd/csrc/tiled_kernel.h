@@ -24,11 +24,14 @@
 // Both of our LDS tiles are K-contiguous (A as [BM][BK], B as [BN][BK]), so
 // either can play X.  B plays X and A plays Y: D[n][m] = C[m][n], and the
 // accumulator layout then gives each lane four consecutive n of one row m of
-// C, which is one 16-byte store into row-major C with no LDS round trip.
+// C (16 bytes).  The epilogue stages C through LDS in row passes so that each
+// store instruction writes whole rows (whole 128-byte lines, with the
+// non-temporal hint).
 //
 // B layouts.  Column-major B (N x K, K contiguous) is staged like A.
-// Row-major B (K x N, N contiguous) is fetched as 16 (k) x 4 (n) byte blocks
-// with dword loads, transposed in registers, and written K-contiguous.
+// Row-major B (K x N, N contiguous) is staged as it lies, BK rows of BN bytes
+// (16-byte chunks permuted by brow_swizzle), and its K-major operands are
+// gathered with the transpose read ds_read_b64_tr_b8 (brow_frag_offsets).
 //
 // FAST = true: no predication; the dispatcher guarantees M % BM == 0,
 // N % BN == 0, K % BK == 0, 16-byte aligned A, B, C and lda, ldb multiples
