@@ -29,7 +29,9 @@
 // form.  There lane (r, g) reads, for the 16 rows k = 64*s + 16*g .. +15,
 // the dword holding columns n0 + 4r .. +3, transposes the 16 x 4 bytes in
 // registers, and feeds column n0 + 4r + j to instruction j (j = 0..3); one
-// block therefore covers 64 columns.  Aligned row-major shapes go to
+// block therefore covers 64 columns.  Aligned row-major shapes go to the
+// column-group form (the split form of the pipelined kernel, see
+// kernel_table.h) when N and K divide into its groups and slices, else to
 // gemm_skinny_rrlds_kernel below.
 #pragma once
 
