@@ -75,6 +75,57 @@ def test_edge_grid_sample_every_config(lib, bcm):
                 check_case(case, f"edge cfg{c.id}", config=c.id)
 
 
+@pytest.mark.parametrize("bcm", [True, False])
+def test_edge_grid_exhaustive_every_config(lib, bcm):
+    """Every compiled configuration on the whole edge grid (M, N in EDGE_MN,
+    K in EDGE_K: 800 shapes).  The operands are top-left corners of one large
+    matrix each, so every row carries real (nonzero) bytes past K (past N for
+    row-major B) that must not enter the sum; lda = 781 and ldb = 781 or 261
+    are not 16-byte multiples.  Each shape writes its own C region (ldc =
+    N + 2) inside one sentinel-filled buffer; the padding and the gaps
+    between regions must survive.  All launches of a configuration go out
+    before one synchronisation."""
+    import oracle
+    t = lib
+    Mx, Kx = max(EDGE_MN), max(EDGE_K)
+    A, B = synthetic.gemm_inputs(Mx, Mx, Kx, seed=77)
+    lda = Kx + 4
+    A_st = np.zeros((Mx, lda), np.int8)
+    A_st[:, :Kx] = A
+    A_st[:, Kx:] = 55
+    Bs = synthetic.store_b(B, bcm)
+    ldb = Bs.shape[1] + 4
+    B_st = np.zeros((Bs.shape[0], ldb), np.int8)
+    B_st[:, :Bs.shape[1]] = Bs
+    B_st[:, Bs.shape[1]:] = -55
+    shapes = [(m, n, k) for m in EDGE_MN for n in EDGE_MN for k in EDGE_K]
+    want, offs, total = {}, {}, 0
+    for (m, n, k) in shapes:
+        want[(m, n, k)] = oracle.gemm(A_st[:m], B_st[:(n if bcm else k)], bcm, M=m, N=n, K=k)
+        offs[(m, n, k)] = total
+        total += m * (n + 2) + 16
+    Ad = torch.from_numpy(A_st).cuda()
+    Bd = torch.from_numpy(B_st).cuda()
+    Cd = torch.empty(total, dtype=torch.int32, device="cuda")
+    for c in table(t):
+        note(f"[case] exhaustive edge grid cfg{c.id} bcm={bcm}")
+        Cd.fill_(-123456789)
+        for (m, n, k) in shapes:
+            st = t.gemm_s8s8s32_with_config(c.id, int(bcm), m, n, k, Ad.data_ptr(), lda, Bd.data_ptr(), ldb,
+                                            Cd.data_ptr() + 4 * offs[(m, n, k)], n + 2, 0)
+            assert st == t.OK, (c.id, m, n, k, t.tdi8_status_string(st))
+        torch.cuda.synchronize()
+        flat = Cd.cpu().numpy()
+        for (m, n, k) in shapes:
+            o = offs[(m, n, k)]
+            reg = flat[o:o + m * (n + 2)].reshape(m, n + 2)
+            if not np.array_equal(reg[:, :n], want[(m, n, k)]):
+                bad = np.argwhere(reg[:, :n] != want[(m, n, k)])
+                raise AssertionError(f"cfg{c.id} {m}x{n}x{k} bcm={bcm}: {len(bad)} mismatches, first {bad[0]}")
+            assert (reg[:, n:] == -123456789).all(), f"cfg{c.id} {m}x{n}x{k}: ldc padding written"
+            assert (flat[o + m * (n + 2):o + m * (n + 2) + 16] == -123456789).all(), f"cfg{c.id} {m}x{n}x{k}: gap written"
+
+
 def test_split_k_deterministic(lib):
     """The K-split form adds partial tiles with atomics in whatever order the
     blocks finish; integer addition makes the bytes identical every time."""
