@@ -75,13 +75,15 @@ def test_edge_grid_sample_every_config(lib, bcm):
                 check_case(case, f"edge cfg{c.id}", config=c.id)
 
 
+@pytest.mark.parametrize("aligned", [False, True])
 @pytest.mark.parametrize("bcm", [True, False])
-def test_edge_grid_exhaustive_every_config(lib, bcm):
+def test_edge_grid_exhaustive_every_config(lib, bcm, aligned):
     """Every compiled configuration on the whole edge grid (M, N in EDGE_MN,
     K in EDGE_K: 800 shapes).  The operands are top-left corners of one large
     matrix each, so every row carries real (nonzero) bytes past K (past N for
-    row-major B) that must not enter the sum; lda = 781 and ldb = 781 or 261
-    are not 16-byte multiples.  Each shape writes its own C region (ldc =
+    row-major B) that must not enter the sum.  Unaligned: lda = 781 and ldb =
+    781 or 261 (predicated kernels throughout); aligned: lda = 784 and ldb =
+    784 or 272, so tile-multiple shapes take the unpredicated kernels.  Each shape writes its own C region (ldc =
     N + 2) inside one sentinel-filled buffer; the padding and the gaps
     between regions must survive.  All launches of a configuration go out
     before one synchronisation."""
@@ -89,12 +91,13 @@ def test_edge_grid_exhaustive_every_config(lib, bcm):
     t = lib
     Mx, Kx = max(EDGE_MN), max(EDGE_K)
     A, B = synthetic.gemm_inputs(Mx, Mx, Kx, seed=77)
-    lda = Kx + 4
+    pad = (lambda w: (w + 15) // 16 * 16 - w) if aligned else (lambda w: 4)
+    lda = Kx + pad(Kx)
     A_st = np.zeros((Mx, lda), np.int8)
     A_st[:, :Kx] = A
     A_st[:, Kx:] = 55
     Bs = synthetic.store_b(B, bcm)
-    ldb = Bs.shape[1] + 4
+    ldb = Bs.shape[1] + pad(Bs.shape[1])
     B_st = np.zeros((Bs.shape[0], ldb), np.int8)
     B_st[:, :Bs.shape[1]] = Bs
     B_st[:, Bs.shape[1]:] = -55
@@ -108,7 +111,7 @@ def test_edge_grid_exhaustive_every_config(lib, bcm):
     Bd = torch.from_numpy(B_st).cuda()
     Cd = torch.empty(total, dtype=torch.int32, device="cuda")
     for c in table(t):
-        note(f"[case] exhaustive edge grid cfg{c.id} bcm={bcm}")
+        note(f"[case] exhaustive edge grid cfg{c.id} bcm={bcm} lda={lda} ldb={ldb}")
         Cd.fill_(-123456789)
         for (m, n, k) in shapes:
             st = t.gemm_s8s8s32_with_config(c.id, int(bcm), m, n, k, Ad.data_ptr(), lda, Bd.data_ptr(), ldb,
