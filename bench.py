@@ -301,7 +301,7 @@ def selector_report(t):
             sets = [(torch.randint(-128, 128, (M, K), dtype=torch.int8, device="cuda"),
                      torch.randint(-128, 128, (N, K) if bcm else (K, N), dtype=torch.int8, device="cuda"),
                      torch.empty((M, N), dtype=torch.int32, device="cuda")) for _ in range(nsets)]
-            cands = [c for c in table if c.family == 0 or (M <= c.block_m)]
+            cands = [c for c in table if c.family == 0 or M <= c.block_m or N <= c.block_n]
             times, ref = {}, None
             for c in [table[pick]] + [c for c in cands if c.id != pick]:
                 args = [(c.id, int(bcm), M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0),

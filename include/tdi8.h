@@ -100,7 +100,7 @@ int gemm_s8s8s32_with_config(int config_id, int b_col_major, int M, int N, int K
  * register-limited active threads per compute unit reach the threshold;
  * keep those launching at least (compute units x resident blocks per compute
  * unit) blocks, or, if none does, every configuration reduced to reuse 1
- * (then, for M <= 32, the skinny family); keep the largest compute-to-memory
+ * (then, for M <= 32 or else N <= 32, the skinny family); keep the largest compute-to-memory
  * ratio BM*BN/(BM+BN); keep the fewest rounds of resident blocks; first in
  * table order.  Host only; pure after the first call's initialisation. */
 int select_tile_config(int M, int N, int K);
@@ -138,7 +138,7 @@ typedef struct {
     int num_cu;                /* compute units */
     int max_threads_per_block;
     int min_active_threads;    /* claim-3 threshold on register-limited active threads per CU */
-    int skinny_max_m;          /* largest M routed to the skinny family */
+    int skinny_max_m;          /* largest M (or, for larger M, N) routed to the skinny family; 0: none */
 } tdi8_hw_info;
 
 typedef struct {

@@ -24,7 +24,7 @@ Derived: block_m_threads = waves_m * mfma_m, block_n_threads = waves_n * mfma_n,
 the block tile BM = block_m_threads * m_tiles and BN = block_n_threads * n_tiles.
 
 Hardware description: num_cu, max_threads_per_block, min_active_threads
-(claim 3's threshold), skinny_max_m (the largest M sent to the skinny family).
+(claim 3's threshold), skinny_max_m (the largest M, or N, sent to the skinny family).
 
 Readings:
   claim 2 (TCU case): block_m_threads and block_n_threads are multiples of the
@@ -42,7 +42,9 @@ Readings:
       block_k, m_tiles = n_tiles = 1) and all are kept.
   skinny route (CDNA4 addition): after that fallback, when m <= skinny_max_m,
       the candidates are instead the skinny family with the smallest block
-      height BM >= m; those reaching Thread_Blocks >= num_cu are kept (all if
+      height BM >= m (else, when n <= skinny_max_m, the smallest block width
+      BN >= n: a skinny block streams the large operand once whichever side
+      is small); those reaching Thread_Blocks >= num_cu are kept (all if
       none), then steps 4 and 5 as below.
   claim 5: the compute-to-memory ratio of a BM x BN tile over a K-tile of
       depth BK is BM*BN*BK / (BM*BK + BK*BN) = BM*BN / (BM + BN) (the B tile's
@@ -212,11 +214,14 @@ def select(m: int, n: int, k: int, hw: Hw, table: list[Cfg]) -> Result:
                 seen.add(d.id)
                 s3.append(d)
         s3 = no_overhang(sorted(s3, key=lambda c: c.id), m, n, table)
-        if m <= hw.skinny_max_m:
-            skinny = [c for c in table if c.family == "skinny" and c.BM >= m and step2_ok(c, hw)]
+        if m <= hw.skinny_max_m or n <= hw.skinny_max_m:
+            # a small m picks by block height, else a small n by block width
+            ext = (lambda c: c.BM) if m <= hw.skinny_max_m else (lambda c: c.BN)
+            small = m if m <= hw.skinny_max_m else n
+            skinny = [c for c in table if c.family == "skinny" and ext(c) >= small and step2_ok(c, hw)]
             if skinny:
-                bm = min(c.BM for c in skinny)
-                skinny = [c for c in skinny if c.BM == bm]
+                e = min(ext(c) for c in skinny)
+                skinny = [c for c in skinny if ext(c) == e]
                 route = 2
                 fill = [c for c in skinny if thread_blocks(c, m, n) >= hw.num_cu]
                 s3 = fill if fill else skinny

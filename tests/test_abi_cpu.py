@@ -168,6 +168,9 @@ def test_mi355x_expectations():
     assert s.route == t.ROUTE_SKINNY and tab[s.id].block_m == 16
     s = t.select_tile_config_for(256, 256, 256, hwc, bpc)
     assert s.route == t.ROUTE_FALLBACK and tab[s.id].m_tiles == tab[s.id].n_tiles == 1
+    # a small N routes to the skinny family by block width
+    s = t.select_tile_config_for(4096, 16, 4096, hwc, bpc)
+    assert s.route == t.ROUTE_SKINNY and tab[s.id].block_n == 16
 
 
 def test_split_k_matches_oracle_reading():

@@ -59,6 +59,16 @@ def test_derived_quantities():
     (33, 4096, 5, 1),
     # 1 x 1: fallback then skinny; nothing fills, keep {6, 7}; ratio picks id7
     (1, 1, 7, 2),
+    # 4096 x 16: M is large, N = 16 small: skinny by block width: smallest BN >= 16 is
+    # 16 (id6 16 x 16, id8 32 x 16); id6 256 x 1 = 256 blocks, id8 128 < 256 -> id6
+    (4096, 16, 6, 2),
+    # 8192 x 16: id6 512 and id8 256 both fill; ratio 32*16/48 > 16*16/32 -> id8
+    (8192, 16, 8, 2),
+    # 4096 x 17: smallest BN >= 17 is 32 -> id7 (16 x 32, 256 blocks)
+    (4096, 17, 7, 2),
+    # 4096 x 33: no skinny width reaches 33 and M > 32: the fallback's pick stands;
+    # step 1 keeps widths <= max(33, 32): id5 only -> id5
+    (4096, 33, 5, 1),
 ])
 def test_worked_examples(m, n, want_id, want_route):
     r = select(m, n, 4096, HW, table())

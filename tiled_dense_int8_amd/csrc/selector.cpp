@@ -15,7 +15,8 @@
 //          step-2 survivor is reduced to reuse 1 (m_tiles = n_tiles = 1: its
 //          reuse-1 sibling) and kept (claim 4).  For M <= skinny_max_m the
 //          candidates then become the skinny family with the smallest block
-//          height >= M, keeping those with at least one block per compute
+//          height >= M (else, for N <= skinny_max_m, with the smallest block
+//          width >= N), keeping those with at least one block per compute
 //          unit (all of them if none has);
 //  step 4  keep the largest compute-to-memory ratio of a K step,
 //          BM*BN*BK / (BM*BK + BK*BN) = BM*BN / (BM + BN), compared exactly
@@ -158,20 +159,27 @@ int select_config(int M, int N, int K, const tdi8_hw_info &hw, const int *bpc, t
             if (taken[id] && fits(static_cfg(id))) sib_fit = true;
         for (int id = 0; id < TDI8_NUM_CONFIGS; ++id)
             if (taken[id] && (!sib_fit || fits(static_cfg(id)))) list[n3++] = Cand{static_cfg(id), bpc[id]};
-        if (M <= hw.skinny_max_m) {
-            int best_bm = 0;
+        // The skinny family covers a small M, or else a small N: its block
+        // extent along that dimension is the smallest one >= it.
+        const bool by_m = M <= hw.skinny_max_m;
+        if (by_m || N <= hw.skinny_max_m) {
+            const int small = by_m ? M : N;
+            auto extent = [&](const StaticCfg &c) { return by_m ? c.bm : c.bn; };
+            int best_ext = 0;
             for (int id = 0; id < TDI8_NUM_CONFIGS; ++id) {
                 const StaticCfg c = static_cfg(id);
-                if (c.family == 1 && c.bm >= M && passes_step2(c, bpc[id], hw) && (best_bm == 0 || c.bm < best_bm))
-                    best_bm = c.bm;
+                if (c.family == 1 && extent(c) >= small && passes_step2(c, bpc[id], hw) &&
+                    (best_ext == 0 || extent(c) < best_ext))
+                    best_ext = extent(c);
             }
-            if (best_bm > 0) {
+            if (best_ext > 0) {
                 route = TDI8_ROUTE_SKINNY;
                 Cand sk[TDI8_NUM_CONFIGS];
                 int nsk = 0, nfill = 0;
                 for (int id = 0; id < TDI8_NUM_CONFIGS; ++id) {
                     const StaticCfg c = static_cfg(id);
-                    if (c.family == 1 && c.bm == best_bm && passes_step2(c, bpc[id], hw)) sk[nsk++] = Cand{c, bpc[id]};
+                    if (c.family == 1 && extent(c) == best_ext && passes_step2(c, bpc[id], hw))
+                        sk[nsk++] = Cand{c, bpc[id]};
                 }
                 for (int i = 0; i < nsk; ++i)
                     if (thread_blocks(sk[i].c, M, N) >= hw.num_cu) list[nfill++] = sk[i];
