@@ -165,21 +165,24 @@ int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, cons
         g.tiles_m = static_cast<int>(tm);
         g.tiles_n = static_cast<int>(tn);
         grid = dim3(static_cast<unsigned>(tm * tn));
-        // both B layouts are moved by 16-byte LDS DMA loads in the fast form
+        // both B layouts are moved by 16-byte LDS DMA loads in the fast form;
+        // a ragged M is fine there (A rows past M read a zero chunk, stores
+        // are masked), a ragged N or K is not
         const bool b_ok = aligned(B, 16) && ldb % 16 == 0;
-        fast = M % c.bm == 0 && N % c.bn == 0 && K % c.bk == 0 && a_ok && b_ok && c_ok;
-        if (fast) g.splits = split_k_for(c, M, N, K, num_cu);
+        fast = N % c.bn == 0 && K % c.bk == 0 && a_ok && b_ok && c_ok;
+        if (fast && M % c.bm == 0) g.splits = split_k_for(c, M, N, K, num_cu);
         if (g.splits > 1)
             return launch_split(kernels()[id].split[bcol ? 1 : 0], g, dim3(static_cast<unsigned>(tm * tn * g.splits)),
                                 block, stream);
     } else {
-        // the unpredicated forms move B by 16-byte LDS DMA loads in both layouts
-        fast = M % c.bm == 0 && N % c.bn == 0 && K % c.bk == 0 && a_ok && aligned(B, 16) && ldb % 16 == 0 && c_ok;
+        // the unpredicated forms move B by 16-byte LDS DMA loads in both
+        // layouts; a ragged M (M < 16 included) reads zero chunks past M
+        fast = N % c.bn == 0 && K % c.bk == 0 && a_ok && aligned(B, 16) && ldb % 16 == 0 && c_ok;
         // Row-major B: the column-group form (kernel_table.h) when its
         // 128-column groups and K slices divide the problem.
         const int groups = kRrGroupCols / c.bn;
         if (!bcol && fast && N % kRrGroupCols == 0 && K % (groups * rr_group_bk(c.bm)) == 0) {
-            const int64_t tm = M / c.bm;
+            const int64_t tm = (M + static_cast<int64_t>(c.bm) - 1) / c.bm;
             const int64_t tn = N / kRrGroupCols;
             if (tm * tn * groups <= INT_MAX / 512) {
                 g.tiles_m = static_cast<int>(tm);

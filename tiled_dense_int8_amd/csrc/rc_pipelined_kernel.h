@@ -141,7 +141,10 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
     const int nk = SRC == 0 ? kslice / BK : (cv.rsc + BK - 1) / BK;
 
     // Per-lane source pointers of this wave's load instructions (K offset 0).
+    // GEMM: A rows past M (the last block row of a ragged M) read the zero
+    // chunk (aok false), so M needs no tile multiple.
     const int8_t *src[LPW];
+    [[maybe_unused]] bool aok[LPW];
     // Convolution: per load slot, the row's base (image or filter), the
     // image position of tap (0, 0), the 16-byte chunk of the K tile, and
     // whether the row exists (output pixel < M, output channel < N).
@@ -174,10 +177,12 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
             }
             continue;
         }
+        aok[i] = true;
         if (q < A_CHUNKS) {
             const int r = q / CPR;
             const int c = (q % CPR) ^ chunk_swizzle<CPR>(r);
-            src[i] = g.A + static_cast<int64_t>(m0 + r) * g.lda + k_begin + 16 * c;
+            aok[i] = m0 + r < g.M;
+            src[i] = g.A + static_cast<int64_t>(aok[i] ? m0 + r : m0) * g.lda + k_begin + 16 * c;
         } else if constexpr (!BROW) {
             const int qb = q - A_CHUNKS;
             const int r = qb / CPR;
@@ -199,7 +204,7 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
     // Source of load slot i for K tile kt.
     auto source = [&](int i, int kt) -> const int8_t * {
         if constexpr (SRC == 0) {
-            return src[i] + koff(i, kt);
+            return aok[i] ? src[i] + koff(i, kt) : zero_chunk;
         } else {
             const bool is_a = (i * NW + wave) * 64 < A_CHUNKS;
             const int kpos = kt * BK + 16 * cch[i];
@@ -446,12 +451,14 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
             for (int idx = threadIdx.x; idx < rows * BN; idx += NW * 64) {
                 const int r = idx / BN;
                 const int c = idx - r * BN;
-                atomicAdd(g.C + static_cast<int64_t>(m0 + p0 + r) * g.ldc + n0 + c, cl[r * RS + c]);
+                if (m0 + p0 + r < g.M)
+                    atomicAdd(g.C + static_cast<int64_t>(m0 + p0 + r) * g.ldc + n0 + c, cl[r * RS + c]);
             }
         }
         return;
     }
 
+    const bool full_rows = m0 + BM <= g.M;  // this block's rows all exist
     if constexpr (MF == 32) {
         // C through LDS (free once the K loop is done), in passes of RP rows
         // as in the split epilogue: a store instruction then covers 64
@@ -491,7 +498,11 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
             for (int idx = threadIdx.x; idx < rows * (BN / 4); idx += NW * 64) {
                 const int r = idx / (BN / 4);
                 const int c4 = idx - r * (BN / 4);
-                store4_nt<SRC == 0>(g, m0 + p0 + r, n0 + 4 * c4, *reinterpret_cast<const i32x4 *>(cl + r * RS + 4 * c4));
+                const i32x4 v = *reinterpret_cast<const i32x4 *>(cl + r * RS + 4 * c4);
+                if (SRC == 0 && full_rows)
+                    store4_nt<true>(g, m0 + p0 + r, n0 + 4 * c4, v);
+                else
+                    store4_nt<false>(g, m0 + p0 + r, n0 + 4 * c4, v);
             }
         }
     } else {
@@ -502,7 +513,10 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
             for (int j = 0; j < NT; ++j) {
                 const int mb = m0 + wm * (MT * MF) + i * MF;
                 const int nb = n0 + wn * (NT * MF) + j * MF;
-                store4<SRC == 0>(g, mb + (lane & 15), nb + 4 * (lane >> 4), acc[i][j]);
+                if (SRC == 0 && full_rows)
+                    store4<true>(g, mb + (lane & 15), nb + 4 * (lane >> 4), acc[i][j]);
+                else
+                    store4<false>(g, mb + (lane & 15), nb + 4 * (lane >> 4), acc[i][j]);
             }
         }
     }

@@ -22,8 +22,8 @@
 // contiguous bytes from each of 16 rows).
 //
 // gemm_skinny_kernel takes column-major B (K-contiguous columns).  FAST:
-// M % (16 MT) == 0, N % (16 NT) == 0, K % 256 == 0, 16-byte aligned A, B, C,
-// lda and ldb multiples of 16, ldc of 4.
+// N % (16 NT) == 0, K % 256 == 0, 16-byte aligned A, B, C, lda and ldb
+// multiples of 16, ldc of 4.
 //
 // gemm_skinny_rr_kernel takes row-major B (N contiguous) in the predicated
 // form.  There lane (r, g) reads, for the 16 rows k = 64*s + 16*g .. +15,
@@ -178,14 +178,17 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
     const int n0 = blockIdx.x * BN;
     const int nch = g.K / KC;
 
+    // A rows past M (a ragged M, e.g. M < 16) read the zero chunk (ok false).
     const int8_t *src[LPW];
     int dst_off[LPW];
+    bool ok[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int x = i * WK + wave;
         const int row = x / PIECES;
         const int piece = x % PIECES;
-        src[i] = (row < BM ? g.A + static_cast<int64_t>(m0 + row) * g.lda
+        ok[i] = row >= BM || m0 + row < g.M;
+        src[i] = (row < BM ? g.A + static_cast<int64_t>(ok[i] ? m0 + row : m0) * g.lda
                            : g.B + static_cast<int64_t>(n0 + row - BM) * g.ldb) + piece * 1024 + 16 * lane;
         dst_off[i] = row * RS + piece * 1024;
     }
@@ -196,11 +199,11 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
     auto issue = [&](int c) {
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
+            const int8_t *p = ok[i] ? src[i] + c * KC : zero_chunk;
             if (b_once && (i * WK + wave) / PIECES >= BM)
-                __builtin_amdgcn_global_load_lds(src[i] + c * KC, (lds_void_t *)(buf[c & 1] + dst_off[i]), 16, 0,
-                                                 kLoadStream);
+                __builtin_amdgcn_global_load_lds(p, (lds_void_t *)(buf[c & 1] + dst_off[i]), 16, 0, kLoadStream);
             else
-                __builtin_amdgcn_global_load_lds(src[i] + c * KC, (lds_void_t *)(buf[c & 1] + dst_off[i]), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(p, (lds_void_t *)(buf[c & 1] + dst_off[i]), 16, 0, 0);
         }
     };
 
@@ -258,7 +261,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
         const i32x4 sum = {red[tile][0][l], red[tile][1][l], red[tile][2][l], red[tile][3][l]};
         const int m = m0 + 16 * (tile / NT) + (l & 15);
         const int n = n0 + 16 * (tile % NT) + 4 * (l >> 4);
-        store4<true>(g, m, n, sum);
+        if (m < g.M) store4<true>(g, m, n, sum);
     }
 #endif
 }
@@ -316,14 +319,16 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
     const int krow = (lane & 7) + 8 * (lane >> 5) + 16 * ((lane >> 3) & 3);
     const int8_t *src[LPW];
     int dst_off[LPW];
-    bool is_b[LPW];
+    bool is_b[LPW], ok[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int x = i * WK + wave;
+        ok[i] = true;
         if (x < A_LOADS) {
             const int row = x / PIECES;
             const int piece = x % PIECES;
-            src[i] = g.A + static_cast<int64_t>(m0 + row) * g.lda + piece * 1024 + 16 * lane;
+            ok[i] = m0 + row < g.M;   // A rows past M read the zero chunk
+            src[i] = g.A + static_cast<int64_t>(ok[i] ? m0 + row : m0) * g.lda + piece * 1024 + 16 * lane;
             dst_off[i] = row * RS + piece * 1024;
             is_b[i] = false;
         } else {
@@ -339,7 +344,8 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const int64_t off = is_b[i] ? static_cast<int64_t>(c) * KC * g.ldb : static_cast<int64_t>(c) * KC;
-            __builtin_amdgcn_global_load_lds(src[i] + off, (lds_void_t *)(buf[c & 1] + dst_off[i]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(ok[i] ? src[i] + off : zero_chunk, (lds_void_t *)(buf[c & 1] + dst_off[i]),
+                                             16, 0, 0);
         }
     };
 
@@ -407,7 +413,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
         const i32x4 sum = {red[tile][0][l], red[tile][1][l], red[tile][2][l], red[tile][3][l]};
         const int m = m0 + 16 * (tile / NT) + (l & 15);
         const int n = n0 + 16 * (tile % NT) + 4 * (l >> 4);
-        store4<true>(g, m, n, sum);
+        if (m < g.M) store4<true>(g, m, n, sum);
     }
 #endif
 }
