@@ -30,8 +30,9 @@
  *   B  column-major:     B(k,j) at B[j*ldb + k],  ldb >= K   (gemm_s8s8s32_bt)
  *   C  row-major:        C(i,j) at C[i*ldc + j],  ldc >= N
  * Any pointer alignment and any leading dimension are accepted; 16-byte
- * aligned operands whose sizes are tile multiples take the unpredicated fast
- * kernels, the rest take the predicated tail kernels.
+ * aligned operands (lda, ldb multiples of 16, ldc of 4) whose N and K are
+ * multiples of the tile's take the unpredicated fast kernels, whatever M; the
+ * rest take the predicated tail kernels.
  *
  * Streams and errors.  Calls are asynchronous: work is enqueued on `stream`
  * (0 = the null stream) and the call returns without waiting.  All argument

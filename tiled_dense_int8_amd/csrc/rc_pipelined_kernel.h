@@ -1,5 +1,6 @@
 // Unpredicated int8 GEMM kernel on gfx950: the form the dispatcher uses when
-// every dimension is a tile multiple and the operands are 16-byte aligned.
+// N and K are tile multiples and the operands are 16-byte aligned (A rows
+// past a ragged M read a zero chunk; their stores are masked).
 // A (row-major) and column-major B are K-contiguous, so their tiles go from
 // HBM to LDS as K-contiguous rows.  Row-major B (BROW) is copied as it lies,
 // BK rows of BN contiguous bytes, and its operand fragments are gathered
