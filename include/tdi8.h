@@ -30,8 +30,10 @@
  *   B  column-major:     B(k,j) at B[j*ldb + k],  ldb >= K   (gemm_s8s8s32_bt)
  *   C  row-major:        C(i,j) at C[i*ldc + j],  ldc >= N
  * Any pointer alignment and any leading dimension are accepted; 16-byte
- * aligned operands (lda, ldb multiples of 16, ldc of 4) whose N and K are
- * multiples of the tile's take the unpredicated fast kernels, whatever M; the
+ * aligned operands (lda, ldb multiples of 16, ldc of 4) with K a multiple of
+ * 16 (and, for row-major B, N a multiple of 16) take the unpredicated fast
+ * kernels, whatever the other sizes: rows, columns and K positions past the
+ * operands read a 16-byte zero block and stores past M or N are masked.  The
  * rest take the predicated tail kernels.
  *
  * Streams and errors.  Calls are asynchronous: work is enqueued on `stream`
@@ -157,9 +159,9 @@ int select_tile_config_for(int M, int N, int K, const tdi8_hw_info *hw,
 
 /* K slices the gemm entry points use with configuration `config_id` for an
  * M x K by K x N product on a device of `num_cu` compute units, when the
- * operands take the unpredicated path (sizes multiples of the block tile,
- * 16-byte aligned pointers, lda and ldb multiples of 16, ldc of 4); other
- * operands are never split.  Splitting K with integer atomics is the contest
+ * operands take the unpredicated path with sizes that are multiples of the
+ * block tile (16-byte aligned pointers, lda and ldb multiples of 16, ldc of
+ * 4); other operands are never split.  Splitting K with integer atomics is the contest
  * write-up's "Split K" paragraph, added after the five steps of the
  * selection: while the tiles times twice the slices still fit one block per
  * compute unit, and each slice stays a whole number of at least four K

@@ -50,6 +50,10 @@ def test_every_config_small_and_ragged(lib, bcm):
 
 EDGE_MN = [1, 15, 16, 17, 31, 32, 33, 255, 256, 257]
 EDGE_K = [0, 1, 4, 27, 63, 64, 65, 777]
+# the exhaustive grid adds multiples of 16 that no tile divides: ragged tiles
+# of the unpredicated kernels
+EXH_MN = EDGE_MN + [48, 272]
+EXH_K = EDGE_K + [16, 48, 752]
 
 
 @pytest.mark.parametrize("bcm", [True, False])
@@ -78,8 +82,8 @@ def test_edge_grid_sample_every_config(lib, bcm):
 @pytest.mark.parametrize("aligned", [False, True])
 @pytest.mark.parametrize("bcm", [True, False])
 def test_edge_grid_exhaustive_every_config(lib, bcm, aligned):
-    """Every compiled configuration on the whole edge grid (M, N in EDGE_MN,
-    K in EDGE_K: 800 shapes).  The operands are top-left corners of one large
+    """Every compiled configuration on the whole edge grid (M, N in EXH_MN,
+    K in EXH_K: 1584 shapes).  The operands are top-left corners of one large
     matrix each, so every row carries real (nonzero) bytes past K (past N for
     row-major B) that must not enter the sum.  Unaligned: lda = 781 and ldb =
     781 or 261 (predicated kernels throughout); aligned: lda = 784 and ldb =
@@ -89,7 +93,7 @@ def test_edge_grid_exhaustive_every_config(lib, bcm, aligned):
     before one synchronisation."""
     import oracle
     t = lib
-    Mx, Kx = max(EDGE_MN), max(EDGE_K)
+    Mx, Kx = max(EXH_MN), max(EXH_K)
     A, B = synthetic.gemm_inputs(Mx, Mx, Kx, seed=77)
     pad = (lambda w: (w + 15) // 16 * 16 - w) if aligned else (lambda w: 4)
     lda = Kx + pad(Kx)
@@ -101,7 +105,7 @@ def test_edge_grid_exhaustive_every_config(lib, bcm, aligned):
     B_st = np.zeros((Bs.shape[0], ldb), np.int8)
     B_st[:, :Bs.shape[1]] = Bs
     B_st[:, Bs.shape[1]:] = -55
-    shapes = [(m, n, k) for m in EDGE_MN for n in EDGE_MN for k in EDGE_K]
+    shapes = [(m, n, k) for m in EXH_MN for n in EXH_MN for k in EXH_K]
     want, offs, total = {}, {}, 0
     for (m, n, k) in shapes:
         want[(m, n, k)] = oracle.gemm(A_st[:m], B_st[:(n if bcm else k)], bcm, M=m, N=n, K=k)

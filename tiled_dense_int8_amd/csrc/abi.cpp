@@ -157,7 +157,7 @@ int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, cons
     const bool c_ok = aligned(C, 16) && ldc % 4 == 0;
     const bool a_ok = aligned(A, 16) && lda % 16 == 0;
     dim3 grid, block(c.threads);
-    bool fast;
+    bool fast, edge = false;
     if (c.family == 0) {
         const int64_t tm = (M + static_cast<int64_t>(c.bm) - 1) / c.bm;
         const int64_t tn = (N + static_cast<int64_t>(c.bn) - 1) / c.bn;
@@ -166,11 +166,14 @@ int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, cons
         g.tiles_n = static_cast<int>(tn);
         grid = dim3(static_cast<unsigned>(tm * tn));
         // both B layouts are moved by 16-byte LDS DMA loads in the fast form;
-        // a ragged M is fine there (A rows past M read a zero chunk, stores
-        // are masked), a ragged N or K is not
+        // chunks outside the operands read a zero chunk and stores are
+        // masked, so M and N are free and K (and, row-major B, N) need only
+        // be multiples of 16 (the edge form: sizes that end inside a tile);
+        // the K split only for whole tiles
         const bool b_ok = aligned(B, 16) && ldb % 16 == 0;
-        fast = N % c.bn == 0 && K % c.bk == 0 && a_ok && b_ok && c_ok;
-        if (fast && M % c.bm == 0) g.splits = split_k_for(c, M, N, K, num_cu);
+        fast = K % 16 == 0 && (bcol || N % 16 == 0) && a_ok && b_ok && c_ok;
+        edge = fast && (M % c.bm != 0 || N % c.bn != 0 || K % c.bk != 0);
+        if (fast && !edge) g.splits = split_k_for(c, M, N, K, num_cu);
         if (g.splits > 1)
             return launch_split(kernels()[id].split[bcol ? 1 : 0], g, dim3(static_cast<unsigned>(tm * tn * g.splits)),
                                 block, stream);
@@ -202,7 +205,7 @@ int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, cons
         g.tiles_n = static_cast<int>(tn);
         grid = dim3(static_cast<unsigned>(tn), static_cast<unsigned>(tm));
     }
-    const void *k = kernels()[id].kernel[bcol ? 1 : 0][fast ? 1 : 0];
+    const void *k = edge ? kernels()[id].edge[bcol ? 1 : 0] : kernels()[id].kernel[bcol ? 1 : 0][fast ? 1 : 0];
     void *args[] = {&g};
     hipError_t e = hipLaunchKernel(k, grid, block, args, 0, stream);
     if (e != hipSuccess) return hip_fail(e);

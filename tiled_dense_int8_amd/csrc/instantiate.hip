@@ -30,7 +30,8 @@ template <class P, bool BCOL, bool FAST>
 static const void *entry() {
     if constexpr (P::family == 0 && FAST)
         return reinterpret_cast<const void *>(
-            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, stages_for<P, BCOL>(), !BCOL, false>);
+            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, stages_for<P, BCOL>(), !BCOL, false,
+                                      false>);
     else if constexpr (P::family == 0)
         return reinterpret_cast<const void *>(
             &gemm_tiled_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, BCOL, FAST>);
@@ -48,7 +49,19 @@ template <class P, bool BCOL>
 static const void *split_entry() {
     if constexpr (P::family == 0)
         return reinterpret_cast<const void *>(
-            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, stages_for<P, BCOL>(), !BCOL, true>);
+            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, stages_for<P, BCOL>(), !BCOL, true,
+                                      false>);
+    else
+        return nullptr;
+}
+
+// The unpredicated general kernel for sizes that end inside a tile.
+template <class P, bool BCOL>
+static const void *edge_entry() {
+    if constexpr (P::family == 0)
+        return reinterpret_cast<const void *>(
+            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, stages_for<P, BCOL>(), !BCOL, false,
+                                      true>);
     else
         return nullptr;
 }
@@ -77,10 +90,10 @@ template <class P>
 static const void *rr_group_entry() {
     if constexpr (P::family == 1 && P::mt == 1) {
         static_assert(rr_group_bk(16) == 512, "K tile of the 16-row form");
-        return reinterpret_cast<const void *>(&gemm_rc_pipelined_kernel<16, 1, 8, 1, 1, 512, 2, true, true>);
+        return reinterpret_cast<const void *>(&gemm_rc_pipelined_kernel<16, 1, 8, 1, 1, 512, 2, true, true, true>);
     } else if constexpr (P::family == 1 && P::mt == 2) {
         static_assert(rr_group_bk(32) == 256, "K tile of the 32-row form");
-        return reinterpret_cast<const void *>(&gemm_rc_pipelined_kernel<16, 1, 8, 2, 1, 256, 3, true, true>);
+        return reinterpret_cast<const void *>(&gemm_rc_pipelined_kernel<16, 1, 8, 2, 1, 256, 3, true, true, true>);
     } else {
         return nullptr;
     }
@@ -94,6 +107,8 @@ void TDI8_CAT(register_cfg_, TDI8_CFG)(KernelSet *ks) {
     ks->kernel[1][1] = entry<P, true, true>();
     ks->split[0] = split_entry<P, false>();
     ks->split[1] = split_entry<P, true>();
+    ks->edge[0] = edge_entry<P, false>();
+    ks->edge[1] = edge_entry<P, true>();
     ks->conv = conv_entry<P>();
     ks->conv_gather = conv_gather_entry<P>();
     ks->rr_group = rr_group_entry<P>();

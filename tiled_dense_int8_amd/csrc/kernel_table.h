@@ -18,12 +18,14 @@ struct CfgParams;
 TDI8_CONFIG_LIST(TDI8_DEFINE_PARAMS)
 #undef TDI8_DEFINE_PARAMS
 
-// kernel[b_col_major][fast]: host stubs of the four instantiations;
-// split[b_col_major]: the K-split form of the fast general kernel (null for
-// the skinny family); conv: the implicit-GEMM convolution form.
+// kernel[b_col_major][fast]: host stubs of the four instantiations (the fast
+// general kernel for whole tiles); split[b_col_major]: its K-split form and
+// edge[b_col_major]: its form for sizes that end inside a tile (null for the
+// skinny family); conv: the implicit-GEMM convolution form.
 struct KernelSet {
     const void *kernel[2][2];
     const void *split[2];
+    const void *edge[2];
     const void *conv;   // implicit-GEMM convolution form (null for the skinny family)
     const void *conv_gather;  // its byte-gather form: any channel count or alignment
     const void *rr_group;  // row-major B column-group form (skinny family only)

@@ -1,6 +1,7 @@
 // Unpredicated int8 GEMM kernel on gfx950: the form the dispatcher uses when
-// N and K are tile multiples and the operands are 16-byte aligned (A rows
-// past a ragged M read a zero chunk; their stores are masked).
+// the operands and leading dimensions are 16-byte aligned and K (and, for
+// row-major B, N) is a multiple of 16: chunks outside the operands read a
+// zero chunk and the stores of a partial tile are masked.
 // A (row-major) and column-major B are K-contiguous, so their tiles go from
 // HBM to LDS as K-contiguous rows.  Row-major B (BROW) is copied as it lies,
 // BK rows of BN contiguous bytes, and its operand fragments are gathered
@@ -86,7 +87,10 @@ constexpr int step_group(int ks, int f) {
 // SPLIT: the grid holds g.splits blocks per tile, slice s of a tile covering
 // K range [s K / splits, (s + 1) K / splits) and adding its partial sums into
 // C (zeroed beforehand) with integer atomics: exact in any order.
-template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW, bool SPLIT, int SRC>
+// EDGE: M, N or K may end inside a tile (chunks outside the operands read the
+// zero chunk, stores are masked); without it M, N and the K extent of a block
+// are whole tiles and the kernel carries none of these tests.
+template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW, bool SPLIT, bool EDGE, int SRC>
 __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvParams &cv) {
     static_assert(SRC == 0 || (!BROW && !SPLIT), "the convolution source is column-major B, unsplit");
     constexpr int NW = WM * WN;
@@ -137,15 +141,20 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
     tile_of_block(g, bid, tm, tn);
     const int m0 = tm * BM;
     const int n0 = tn * BN;
-    // GEMM: K is a multiple of BK.  Convolution: the reduction R*S*C is a
-    // multiple of 16 and its last K tile is completed with zero chunks.
-    const int nk = SRC == 0 ? kslice / BK : (cv.rsc + BK - 1) / BK;
+    // GEMM: K is a multiple of 16 (of BK without EDGE); a last partial K tile
+    // is completed with zero chunks.  Convolution: the reduction R*S*C is a
+    // multiple of 16, completed the same way.
+    const int nk = SRC == 0 ? (kslice + BK - 1) / BK : (cv.rsc + BK - 1) / BK;
 
     // Per-lane source pointers of this wave's load instructions (K offset 0).
-    // GEMM: A rows past M (the last block row of a ragged M) read the zero
-    // chunk (aok false), so M needs no tile multiple.
+    // GEMM: chunks outside the operands read the zero chunk: A rows past M,
+    // column-major B rows past N, row-major B columns past N, and chunks at
+    // or past K.  One comparison covers all of them: the chunk of slot i in
+    // K tile kt exists iff kt * BK < klim[i], with klim[i] = K minus the
+    // chunk's K offset within a tile for a row or column that exists, else 0.
+    // So only N (row-major B) and K need be multiples of 16 (EDGE forms).
     const int8_t *src[LPW];
-    [[maybe_unused]] bool aok[LPW];
+    [[maybe_unused]] int klim[LPW];
     // Convolution: per load slot, the row's base (image or filter), the
     // image position of tap (0, 0), the 16-byte chunk of the K tile, and
     // whether the row exists (output pixel < M, output channel < N).
@@ -178,23 +187,27 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
             }
             continue;
         }
-        aok[i] = true;
         if (q < A_CHUNKS) {
             const int r = q / CPR;
             const int c = (q % CPR) ^ chunk_swizzle<CPR>(r);
-            aok[i] = m0 + r < g.M;
-            src[i] = g.A + static_cast<int64_t>(aok[i] ? m0 + r : m0) * g.lda + k_begin + 16 * c;
+            const bool ok = !EDGE || m0 + r < g.M;
+            klim[i] = ok ? kslice - 16 * c : 0;
+            src[i] = g.A + static_cast<int64_t>(ok ? m0 + r : m0) * g.lda + k_begin + 16 * c;
         } else if constexpr (!BROW) {
             const int qb = q - A_CHUNKS;
             const int r = qb / CPR;
             const int c = (qb % CPR) ^ chunk_swizzle<CPR>(r);
-            src[i] = g.B + static_cast<int64_t>(n0 + r) * g.ldb + k_begin + 16 * c;
+            const bool ok = !EDGE || n0 + r < g.N;
+            klim[i] = ok ? kslice - 16 * c : 0;
+            src[i] = g.B + static_cast<int64_t>(ok ? n0 + r : n0) * g.ldb + k_begin + 16 * c;
         } else {
             // row-major B: LDS row k of the tile holds B(k0 + k, n0 .. n0+BN-1)
             const int qb = q - A_CHUNKS;
             const int k = qb / CPRB;
             const int c = (qb % CPRB) ^ brow_swizzle<BN>(k);
-            src[i] = g.B + (k_begin + k) * g.ldb + n0 + 16 * c;
+            const bool ok = !EDGE || n0 + 16 * c < g.N;
+            klim[i] = ok ? kslice - k : 0;
+            src[i] = g.B + (k_begin + k) * g.ldb + (ok ? n0 + 16 * c : n0);
         }
     }
     // K offset of tile kt for load instruction i.
@@ -204,8 +217,10 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
     };
     // Source of load slot i for K tile kt.
     auto source = [&](int i, int kt) -> const int8_t * {
-        if constexpr (SRC == 0) {
-            return aok[i] ? src[i] + koff(i, kt) : zero_chunk;
+        if constexpr (SRC == 0 && EDGE) {
+            return kt * BK < klim[i] ? src[i] + koff(i, kt) : zero_chunk;
+        } else if constexpr (SRC == 0) {
+            return src[i] + koff(i, kt);
         } else {
             const bool is_a = (i * NW + wave) * 64 < A_CHUNKS;
             const int kpos = kt * BK + 16 * cch[i];
@@ -452,14 +467,14 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
             for (int idx = threadIdx.x; idx < rows * BN; idx += NW * 64) {
                 const int r = idx / BN;
                 const int c = idx - r * BN;
-                if (m0 + p0 + r < g.M)
+                if (!EDGE || m0 + p0 + r < g.M)
                     atomicAdd(g.C + static_cast<int64_t>(m0 + p0 + r) * g.ldc + n0 + c, cl[r * RS + c]);
             }
         }
         return;
     }
 
-    const bool full_rows = m0 + BM <= g.M;  // this block's rows all exist
+    const bool full_rows = !EDGE || (m0 + BM <= g.M && n0 + BN <= g.N);  // the whole tile exists
     if constexpr (MF == 32) {
         // C through LDS (free once the K loop is done), in passes of RP rows
         // as in the split epilogue: a store instruction then covers 64
@@ -524,9 +539,9 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
 #endif
 }
 
-template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW, bool SPLIT>
+template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW, bool SPLIT, bool EDGE>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArgs g) {
-    pipelined_body<MF, WM, WN, MT, NT, BK, STAGES, BROW, SPLIT, 0>(g, ConvParams{});
+    pipelined_body<MF, WM, WN, MT, NT, BK, STAGES, BROW, SPLIT, EDGE, 0>(g, ConvParams{});
 }
 
 // Implicit-GEMM convolution ("先导杯比赛回顾", 卷积转化: the convolution
@@ -539,7 +554,7 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArg
 // rows past M or N read a zero chunk instead.
 template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES>
 __global__ void __launch_bounds__(WM * WN * 64) conv_implicit_kernel(GemmArgs g, ConvParams cv) {
-    pipelined_body<MF, WM, WN, MT, NT, BK, STAGES, false, false, 1>(g, cv);
+    pipelined_body<MF, WM, WN, MT, NT, BK, STAGES, false, false, true, 1>(g, cv);
 }
 
 }  // namespace tdi8
