@@ -109,11 +109,7 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
     static_assert(A_CHUNKS % 64 == 0, "A region must be whole wave instructions");
     static_assert(STAGES >= 2, "at least two stages");
     static_assert(KS % 2 == 0, "operand double buffer needs an even number of K steps per tile");
-#ifdef TDI8_EXP_NO_GROUP
-    constexpr int G = 1;
-#else
     constexpr int G = step_group(KS, MT * NT);   // K steps per operand group
-#endif
     constexpr int KG = KS / G;                   // groups per K tile
     static_assert(KG % 2 == 0, "operand double buffer needs an even number of groups per tile");
     constexpr int CPRB = BN / 16;                // 16-byte chunks per row-major B row
