@@ -120,7 +120,10 @@ typedef struct {
     int stages;          /* LDS stages of the unpredicated column-major-B kernel */
     int threads;
     int lds_bytes;       /* static LDS per block of that kernel */
-    int vgprs, agprs;    /* per lane, from the compiled kernel (0 before a device is seen) */
+    int vgprs;           /* vector registers per lane of the compiled kernel, architectural and
+                            accumulation registers together (the runtime's unified count; 0
+                            before a device is seen) */
+    int agprs;           /* 0: the runtime reports no separate accumulation-register count */
     int blocks_per_cu;   /* resident blocks per compute unit, from the occupancy query */
     int reuse1_id;       /* configuration with the same thread split and m_tiles = n_tiles = 1 */
     int excluded;        /* 1: its reuse scheme (family, m_tiles, n_tiles) was excluded by the
