@@ -217,3 +217,28 @@ def test_conv_validation_and_extent():
     # entry points reject before any device work
     assert t.conv2d_s8s8s32_nhwc(*good, A16, A16 + (1 << 16), A16 + (1 << 17) + 2, 0) == t.ERR_INVALID_VALUE
     assert t.conv2d_s8s8s32_nhwc_with_config(99, *good, A16, A16 + (1 << 16), A16 + (1 << 17), 0) == t.ERR_BAD_CONFIG
+
+
+def test_torch_wrappers_refuse_host_tensors_and_bad_arguments():
+    """The torch wrappers check their tensors before anything reaches the
+    library: host tensors (whose data pointers the kernels would read as
+    device addresses), wrong dtypes, mismatched shapes."""
+    import torch
+    A = torch.zeros((4, 8), dtype=torch.int8)
+    B = torch.zeros((8, 4), dtype=torch.int8)
+    with pytest.raises(ValueError, match="GPU"):
+        t.gemm(A, B, False)
+    with pytest.raises(TypeError):
+        t.gemm(A.to(torch.int16), B, False)
+    with pytest.raises(ValueError, match="inner"):
+        t.gemm(A, B[:4], False)
+    x = torch.zeros((1, 5, 5, 16), dtype=torch.int8)
+    w = torch.zeros((8, 3, 3, 16), dtype=torch.int8)
+    with pytest.raises(ValueError, match="GPU"):
+        t.conv2d(x, w, (1, 1))
+    with pytest.raises(TypeError):
+        t.conv2d(x.to(torch.int32), w, (1, 1))
+    with pytest.raises(ValueError, match="channel"):
+        t.conv2d(x, w[..., :8].contiguous(), (1, 1))
+    with pytest.raises(ValueError, match="contiguous"):
+        t.conv2d(x.permute(0, 2, 1, 3), w, (1, 1))

@@ -155,6 +155,17 @@ def _stream_handle(stream) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _device_of(*tensors) -> "torch.device":
+    """The one GPU holding every tensor (the kernels dereference their data
+    pointers as device addresses, so host tensors must never reach them)."""
+    devs = {t.device for t in tensors}
+    if any(d.type != "cuda" for d in devs):
+        raise ValueError("tensors must be on a GPU")
+    if len(devs) != 1:
+        raise ValueError(f"tensors are on different devices: {sorted(str(d) for d in devs)}")
+    return devs.pop()
+
+
 def gemm(A: "torch.Tensor", B: "torch.Tensor", b_col_major: bool, out: "torch.Tensor | None" = None,
          config: int | None = None, stream=None) -> "torch.Tensor":
     """C = A x B on the GPU.
@@ -173,18 +184,20 @@ def gemm(A: "torch.Tensor", B: "torch.Tensor", b_col_major: bool, out: "torch.Te
     N = B.shape[0] if b_col_major else B.shape[1]
     if (B.shape[1] if b_col_major else B.shape[0]) != K:
         raise ValueError("inner dimensions differ")
+    dev = _device_of(A, B) if out is None else _device_of(A, B, out)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.int32, device=A.device)
+        out = torch.empty((M, N), dtype=torch.int32, device=dev)
     if out.dtype != torch.int32 or out.dim() != 2 or tuple(out.shape) != (M, N) or out.stride(1) != 1:
         raise ValueError("out must be int32 (M, N) with unit column stride")
     lda, ldb, ldc = max(A.stride(0), 1), max(B.stride(0), 1), max(out.stride(0), 1)
-    s = _stream_handle(stream)
-    if config is None:
-        fn = gemm_s8s8s32_bt if b_col_major else gemm_s8s8s32
-        st = fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, s)
-    else:
-        st = gemm_s8s8s32_with_config(config, b_col_major, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
-                                      out.data_ptr(), ldc, s)
+    with torch.cuda.device(dev):
+        s = _stream_handle(stream)
+        if config is None:
+            fn = gemm_s8s8s32_bt if b_col_major else gemm_s8s8s32
+            st = fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, s)
+        else:
+            st = gemm_s8s8s32_with_config(config, b_col_major, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                                          out.data_ptr(), ldc, s)
     if st != OK:
         raise TDI8Error(st)
     return out
@@ -219,18 +232,27 @@ def conv2d_validate(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h
 def conv2d(x, w, pad=(0, 0), stride=(1, 1), dil=(1, 1), out=None, config=None, stream=None):
     """y = conv2d(x, w) for torch tensors on the GPU: x int8 N x H x W x C,
     w int8 K x R x S x C (both contiguous), y int32 N x P x Q x K."""
+    if x.dtype != torch.int8 or w.dtype != torch.int8:
+        raise TypeError("x and w must be int8")
+    if x.dim() != 4 or w.dim() != 4 or not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError("x (N, H, W, C) and w (K, R, S, C) must be contiguous 4-D tensors")
     N, H, W, C = x.shape
-    K, R, S, _ = w.shape
+    K, R, S, Cw = w.shape
+    if Cw != C:
+        raise ValueError(f"channel counts differ: x has {C}, w has {Cw}")
     P = conv2d_output_extent(H, R, pad[0], stride[0], dil[0])
     Q = conv2d_output_extent(W, S, pad[1], stride[1], dil[1])
     if P < 0 or Q < 0:
         raise TDI8Error(min(P, Q))
+    dev = _device_of(x, w) if out is None else _device_of(x, w, out)
     if out is None:
-        out = torch.empty((N, P, Q, K), dtype=torch.int32, device=x.device)
-    sh = torch.cuda.current_stream().cuda_stream if stream is None else stream
-    args = (N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0], dil[1],
-            x.data_ptr(), w.data_ptr(), out.data_ptr(), sh)
-    st = conv2d_s8s8s32_nhwc(*args) if config is None else conv2d_s8s8s32_nhwc_with_config(config, *args)
+        out = torch.empty((N, P, Q, K), dtype=torch.int32, device=dev)
+    if out.dtype != torch.int32 or tuple(out.shape) != (N, P, Q, K) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous int32 tensor of shape {(N, P, Q, K)}")
+    with torch.cuda.device(dev):
+        args = (N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0], dil[1],
+                x.data_ptr(), w.data_ptr(), out.data_ptr(), _stream_handle(stream))
+        st = conv2d_s8s8s32_nhwc(*args) if config is None else conv2d_s8s8s32_nhwc_with_config(config, *args)
     if st != OK:
         raise TDI8Error(st)
     return out
