@@ -78,6 +78,36 @@ def traffic_for(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def counters_for(workload: str):
+    """Matrix-core utilisation, clock and wait share of the workload's kernel
+    from the committed rocprofv3 --pmc summary, if it was taken on the current
+    kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return {k: rec.get(k) for k in ("mfma_busy_frac", "clock_ghz", "waitcnt_wave_frac", "source")}
+
+
+def device_info():
+    """Name, architecture, compute units and the runtime's peak engine clock
+    of device 0 (hipDeviceGetAttribute, attribute 5 = hipDeviceAttributeClockRate
+    in hip_runtime_api.h, in kHz), looked up through the library's own handle
+    so that it is the HIP runtime the library runs on."""
+    import ctypes
+    import torch
+    import tiled_dense_int8_amd as t
+    props = torch.cuda.get_device_properties(0)
+    v = ctypes.c_int(0)
+    fn = t._lib.hipDeviceGetAttribute
+    fn.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    peak_mhz = v.value // 1000 if fn(ctypes.byref(v), 5, 0) == 0 else None
+    return {"name": props.name, "arch": props.gcnArchName, "compute_units": props.multi_processor_count,
+            "peak_sclk_mhz": peak_mhz}
+
+
 def make_sets(w, nsets, seed=0):
     import torch
     import synthetic
@@ -479,6 +509,8 @@ def main():
                      "frac": round(achieved / MFMA_PEAK_TOPS, 4), "traffic": traffic_for(args.workload)},
         "warm": {"kernel_ms": round(warm_ms, 6), "achieved": round(ops / (warm_ms * 1e-3) / 1e12, 3),
                  "note": "one input set reused (A and B cache-resident); value and roofline above are cold"},
+        "counters": counters_for(args.workload),
+        "device": device_info(),
     }
     if args.workload in ("skinny16", "ragged", "single256"):
         byts = M * K + K * N + 4 * M * N
@@ -500,7 +532,8 @@ def main():
                             "ms_per_step": round(s_wall, 6), "freivalds_check": s_ok,
                             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                         "traffic": traffic_for("skinny16")}}
+                                         "traffic": traffic_for("skinny16")},
+                            "counters": counters_for("skinny16")}
         del ssets
 
     if not args.no_cpu_baseline:
