@@ -1,0 +1,62 @@
+"""Seeded random parity cases through the C ABI: shapes drawn to land on,
+next to and between tile multiples, random leading-dimension padding
+(aligned or not), random byte offsets of the operands, both B layouts, the
+selected entry points and forced configurations.  Bit-exact against the
+oracle; C's padding and the canary after it must keep their sentinel."""
+import numpy as np
+import pytest
+
+import synthetic
+from helpers import DeviceCase, check_case
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiled_dense_int8_amd as t
+    return t
+
+
+def draw_dim(rng, hi):
+    kind = rng.integers(0, 5)
+    if kind == 0:
+        return int(rng.integers(1, 33))                  # skinny range
+    if kind == 1:
+        return int(16 * rng.integers(1, hi // 16 + 1))   # multiple of 16
+    if kind == 2:
+        m = int(64 * rng.integers(1, hi // 64 + 1))       # next to a tile multiple
+        return max(1, m + int(rng.integers(-1, 2)))
+    return int(rng.integers(1, hi + 1))
+
+
+def draw_case(rng, bcm):
+    M, N, K = draw_dim(rng, 600), draw_dim(rng, 600), draw_dim(rng, 800)
+    aligned = rng.random() < 0.5
+    if aligned:
+        pad = lambda: int(16 * rng.integers(0, 3))
+        offs = tuple(int(16 * rng.integers(0, 2)) for _ in range(2)) + (int(4 * rng.integers(0, 2)),)
+    else:
+        pad = lambda: int(rng.integers(0, 40))
+        offs = tuple(int(rng.integers(0, 16)) for _ in range(3))
+    lda = K + pad()
+    ldb = (K if bcm else N) + pad()
+    ldc = N + (int(4 * rng.integers(0, 3)) if aligned else int(rng.integers(0, 9)))
+    return M, N, K, lda, ldb, ldc, offs
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_random_shapes_layouts_and_entries(lib, bcm):
+    t = lib
+    n_cfg = t.tile_config_count()
+    rng = np.random.default_rng(20261202 + (1 if bcm else 0))
+    for i in range(160):
+        M, N, K, lda, ldb, ldc, offs = draw_case(rng, bcm)
+        A, B = synthetic.gemm_inputs(M, N, K, seed=1000 + i)
+        case = DeviceCase(A, B, bcm, lda=lda, ldb=ldb, ldc=ldc, offsets=offs)
+        config = None if rng.random() < 0.6 else int(rng.integers(0, n_cfg))
+        check_case(case, f"random[{i}] offs={offs}", config=config)
