@@ -60,3 +60,32 @@ def test_random_shapes_layouts_and_entries(lib, bcm):
         case = DeviceCase(A, B, bcm, lda=lda, ldb=ldb, ldc=ldc, offsets=offs)
         config = None if rng.random() < 0.6 else int(rng.integers(0, n_cfg))
         check_case(case, f"random[{i}] offs={offs}", config=config)
+
+
+def test_random_convolutions(lib):
+    """Seeded random convolution geometries (channels on both sides of the
+    16-channel DMA form, padding, stride, dilation, filters up to 5 x 5),
+    compared in full with the convolution oracle."""
+    import oracle
+    from test_gpu_conv import run_conv
+    t = lib
+    rng = np.random.default_rng(20261203)
+    done = 0
+    while done < 80:
+        N = int(rng.integers(1, 4))
+        H, W = int(rng.integers(1, 21)), int(rng.integers(1, 21))
+        C = int(rng.choice([1, 3, 5, 8, 16, 17, 32, 48, 64]))
+        K = int(rng.integers(1, 71))
+        R, S = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        pad = (int(rng.integers(0, 3)), int(rng.integers(0, 3)))
+        stride = (int(rng.integers(1, 4)), int(rng.integers(1, 4)))
+        dil = (int(rng.integers(1, 3)), int(rng.integers(1, 3)))
+        if oracle.conv_out_extent(H, R, pad[0], stride[0], dil[0]) < 1 or \
+                oracle.conv_out_extent(W, S, pad[1], stride[1], dil[1]) < 1:
+            continue
+        x, w = synthetic.conv_inputs(N, H, W, C, K, R, S, 500 + done)
+        y, tail_ok = run_conv(t, x, w, pad, stride, dil, None, f"random[{done}]")
+        want = oracle.conv2d(x, w, pad, stride, dil)
+        assert np.array_equal(y, want), f"random[{done}]: {int((y != want).sum())} mismatches"
+        assert tail_ok, f"random[{done}]: output tail overwritten"
+        done += 1
