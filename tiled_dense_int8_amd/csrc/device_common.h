@@ -34,6 +34,7 @@ struct ConvParams {
     int sh, sw, ph, pw, dh, dw;
     int rsc;
     FastDiv c_div, s_div;
+    int tile_in_tap;  // C a multiple of the K tile: every K tile lies within one tap
 };
 
 // Division by a divisor d >= 1 fixed for the whole launch, for 0 <= n < 2^31

@@ -222,10 +222,21 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
             const int kpos = kt * BK + 16 * cch[i];
             if (!cok[i] || kpos >= cv.rsc) return zero_chunk;
             if (!is_a) return src[i] + kpos;
-            const int rs = fast_div(kpos, cv.c_div);
-            const int c0 = kpos - rs * cv.C;
-            const int r = fast_div(rs, cv.s_div);
-            const int ss = rs - r * cv.S;
+            int c0, r, ss;
+            if (cv.tile_in_tap) {
+                // The whole K tile lies within one tap: its position (r, s)
+                // is the same for every lane (scalar work); a lane adds only
+                // its chunk's channel offset.
+                const int tap = fast_div(kt * BK, cv.c_div);
+                c0 = kt * BK - tap * cv.C + 16 * cch[i];
+                r = fast_div(tap, cv.s_div);
+                ss = tap - r * cv.S;
+            } else {
+                const int rs = fast_div(kpos, cv.c_div);
+                c0 = kpos - rs * cv.C;
+                r = fast_div(rs, cv.s_div);
+                ss = rs - r * cv.S;
+            }
             const int ih = cih[i] + r * cv.dh;
             const int iw = ciw[i] + ss * cv.dw;
             if (static_cast<unsigned>(ih) >= static_cast<unsigned>(cv.H) ||
