@@ -35,6 +35,7 @@ struct ConvParams {
     int rsc;
     FastDiv c_div, s_div;
     int tile_in_tap;  // C a multiple of the K tile: every K tile lies within one tap
+    int run;          // byte-gather form with S C <= 16 and dw = 1: S C (else 0), see conv_run16
 };
 
 // Division by a divisor d >= 1 fixed for the whole launch, for 0 <= n < 2^31
@@ -65,6 +66,21 @@ __device__ __forceinline__ i32x4 load16(const int8_t *p) {
 // Keep the low `nvalid` bytes (0..4) of a dword.
 __device__ __forceinline__ uint32_t keep_bytes(uint32_t w, int nvalid) {
     return nvalid >= 4 ? w : (nvalid <= 0 ? 0u : (w & ((1u << (8 * nvalid)) - 1u)));
+}
+
+// v with every byte moved up by n bytes (byte i to i + n, zeros below;
+// 0 <= n < 16).
+__device__ __forceinline__ i32x4 shift_up_bytes(i32x4 v, int n) {
+    const uint64_t lo = static_cast<uint32_t>(v[0]) | (static_cast<uint64_t>(static_cast<uint32_t>(v[1])) << 32);
+    const uint64_t hi = static_cast<uint32_t>(v[2]) | (static_cast<uint64_t>(static_cast<uint32_t>(v[3])) << 32);
+    const int b = 8 * n;
+    uint64_t nlo = 0, nhi = lo << (b >= 64 ? b - 64 : 0);
+    if (b < 64) {
+        nlo = lo << b;
+        nhi = b == 0 ? hi : (hi << b) | (lo >> (64 - b));
+    }
+    return i32x4{static_cast<int32_t>(static_cast<uint32_t>(nlo)), static_cast<int32_t>(nlo >> 32),
+                 static_cast<int32_t>(static_cast<uint32_t>(nhi)), static_cast<int32_t>(nhi >> 32)};
 }
 
 // 16 bytes at p, any alignment: one global_load_dwordx4 (the ROCm driver

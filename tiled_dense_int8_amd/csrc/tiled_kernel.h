@@ -147,6 +147,24 @@ __device__ __forceinline__ i32x4 conv_gather16(const int8_t *img, int ih0, int i
     return i32x4{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]), static_cast<int>(w[3])};
 }
 
+// Run form of the gather (cv.run = S C <= 16, dw = 1): the reduction is
+// taken as R runs of 16 positions, run r holding the S C bytes of filter row
+// r (taps s = 0 .. S-1, channels c) and zeros after them.  For one output
+// pixel those bytes lie contiguously in image row ih0 + r dh from column
+// iw0, so a run is one masked load of its taps inside the image (the dword
+// reads of load16_masked stay on the pages of the wanted bytes) moved up to
+// the first such tap; taps outside the image and rows outside it are 0.
+__device__ __forceinline__ i32x4 conv_run16(const int8_t *img, int ih0, int iw0, int kk, const ConvParams &cv) {
+    const int r = kk >> 4;
+    const int ih = ih0 + r * cv.dh;
+    if (r >= cv.R || static_cast<unsigned>(ih) >= static_cast<unsigned>(cv.H)) return i32x4{0, 0, 0, 0};
+    const int s_lo = iw0 < 0 ? -iw0 : 0;                  // first tap inside the image
+    const int s_hi = cv.W - iw0 < cv.S ? cv.W - iw0 : cv.S;  // one past the last
+    if (s_hi <= s_lo) return i32x4{0, 0, 0, 0};
+    const int8_t *p = img + (static_cast<int64_t>(ih) * cv.W + iw0 + s_lo) * cv.C;
+    return shift_up_bytes(load16_masked(p, (s_hi - s_lo) * cv.C), s_lo * cv.C);
+}
+
 // SRC 0: the product of the operands described by g.  SRC 1: implicit-GEMM
 // convolution (A rows gathered from the NHWC image by conv_gather16, B the
 // KRSC filters as column-major K x R S C, C the N P Q x K output).
@@ -219,7 +237,9 @@ __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &
                 const int row = m0 + r;
                 const int kk = k0 + 16 * c;
                 if constexpr (SRC == 1) {
-                    ra[i] = cimg[i] ? conv_gather16(cimg[i], cih[i], ciw[i], kk, cv) : i32x4{0, 0, 0, 0};
+                    ra[i] = !cimg[i] ? i32x4{0, 0, 0, 0}
+                            : cv.run ? conv_run16(cimg[i], cih[i], ciw[i], kk, cv)
+                                     : conv_gather16(cimg[i], cih[i], ciw[i], kk, cv);
                 } else {
                     const int8_t *p = g.A + static_cast<int64_t>(row) * g.lda + kk;
                     ra[i] = FAST ? load16(p) : load16_masked(p, row < g.M ? clamp16(g.K - kk) : 0);
@@ -235,8 +255,14 @@ __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &
                     const int c = (q % CPR) ^ chunk_swizzle<CPR>(r);
                     const int col = n0 + r;
                     const int kk = k0 + 16 * c;
-                    const int8_t *p = g.B + static_cast<int64_t>(col) * g.ldb + kk;
-                    rb[i] = FAST ? load16(p) : load16_masked(p, col < g.N ? clamp16(g.K - kk) : 0);
+                    if (SRC == 1 && cv.run) {
+                        // run form: filter row kk / 16 of output channel col
+                        const int8_t *p = g.B + static_cast<int64_t>(col) * g.ldb + (kk >> 4) * cv.run;
+                        rb[i] = load16_masked(p, col < g.N && kk < g.K ? cv.run : 0);
+                    } else {
+                        const int8_t *p = g.B + static_cast<int64_t>(col) * g.ldb + kk;
+                        rb[i] = FAST ? load16(p) : load16_masked(p, col < g.N ? clamp16(g.K - kk) : 0);
+                    }
                 }
             }
         } else {
