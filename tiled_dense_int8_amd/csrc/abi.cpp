@@ -262,7 +262,7 @@ int conv_check(const ConvShape &c, const int8_t *x, const int8_t *w, const int32
     g->splits = 1;
     *cv = ConvParams{c.N, c.H, c.W, c.C, c.R, c.S, static_cast<int>(P), static_cast<int>(Q),
                      c.sh, c.sw, c.ph, c.pw, c.dh, c.dw, static_cast<int>(rsc),
-                     make_fast_div(c.C > 0 ? c.C : 1), make_fast_div(c.S), 0, 0};
+                     make_fast_div(c.C > 0 ? c.C : 1), make_fast_div(c.S), 0, 0, 1, make_fast_div(1)};
     if (M == 0 || c.K == 0) return TDI8_OK;
     if (!y) return TDI8_ERR_NULL_POINTER;
     if (!aligned(y, 4)) return TDI8_ERR_INVALID_VALUE;
@@ -305,11 +305,17 @@ int conv_entry(int cfg, const ConvShape &c, const int8_t *x, const int8_t *w, in
     // 16-byte aligned operands; otherwise the byte-gather form.
     const bool dma = c.C % 16 == 0 && aligned(x, 16) && aligned(w, 16);
     cv.tile_in_tap = dma && c.C % sc.bk == 0;
-    // byte-gather form with short filter rows: the run form (conv_run16),
-    // whose reduction is R runs of 16 positions
-    if (!dma && c.dw == 1 && c.S * c.C <= 16) {
-        cv.run = c.S * c.C;
-        g.K = c.R * 16;
+    // gather form without horizontal dilation: the run form (conv_run16),
+    // whose reduction is R filter rows of ceil(S C / 16) 16-byte pieces
+    if (!dma && c.dw == 1) {
+        const int64_t run = static_cast<int64_t>(c.S) * c.C;
+        const int64_t runp = (run + 15) / 16;
+        if (c.R * runp * 16 <= INT_MAX) {
+            cv.run = static_cast<int>(run);
+            cv.runp = static_cast<int>(runp);
+            cv.runp_div = make_fast_div(cv.runp);
+            g.K = static_cast<int>(c.R * runp * 16);
+        }
     }
     void *args[] = {&g, &cv};
     hipError_t e = hipLaunchKernel(dma ? kernels()[id].conv : kernels()[id].conv_gather,

@@ -35,7 +35,9 @@ struct ConvParams {
     int rsc;
     FastDiv c_div, s_div;
     int tile_in_tap;  // C a multiple of the K tile: every K tile lies within one tap
-    int run;          // byte-gather form with S C <= 16 and dw = 1: S C (else 0), see conv_run16
+    int run;          // gather form with dw = 1: S C, the bytes of a filter row (else 0), see conv_run16
+    int runp;         // 16-byte pieces per filter row, ceil(S C / 16)
+    FastDiv runp_div;
 };
 
 // Division by a divisor d >= 1 fixed for the whole launch, for 0 <= n < 2^31

@@ -147,22 +147,28 @@ __device__ __forceinline__ i32x4 conv_gather16(const int8_t *img, int ih0, int i
     return i32x4{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]), static_cast<int>(w[3])};
 }
 
-// Run form of the gather (cv.run = S C <= 16, dw = 1): the reduction is
-// taken as R runs of 16 positions, run r holding the S C bytes of filter row
-// r (taps s = 0 .. S-1, channels c) and zeros after them.  For one output
-// pixel those bytes lie contiguously in image row ih0 + r dh from column
-// iw0, so a run is one masked load of its taps inside the image (the dword
-// reads of load16_masked stay on the pages of the wanted bytes) moved up to
-// the first such tap; taps outside the image and rows outside it are 0.
+// Run form of the gather (dw = 1): filter row r's run of S C bytes (taps
+// s = 0 .. S-1, channels c) is padded to runp 16-byte pieces, so the
+// reduction is R runp pieces and position kk is byte 16 j + kk % 16 of run r,
+// with kk / 16 = r runp + j.  For one output pixel a run lies contiguously in
+// image row ih0 + r dh from column iw0, so a piece is one masked load of its
+// bytes that belong to taps inside the image (the dword reads of
+// load16_masked stay on the pages of the wanted bytes) moved up to its place;
+// taps outside the image, rows outside it and the padding are 0.
 __device__ __forceinline__ i32x4 conv_run16(const int8_t *img, int ih0, int iw0, int kk, const ConvParams &cv) {
-    const int r = kk >> 4;
+    const int pi = kk >> 4;
+    const int r = fast_div(pi, cv.runp_div);
+    const int j16 = 16 * (pi - r * cv.runp);
     const int ih = ih0 + r * cv.dh;
     if (r >= cv.R || static_cast<unsigned>(ih) >= static_cast<unsigned>(cv.H)) return i32x4{0, 0, 0, 0};
     const int s_lo = iw0 < 0 ? -iw0 : 0;                  // first tap inside the image
     const int s_hi = cv.W - iw0 < cv.S ? cv.W - iw0 : cv.S;  // one past the last
-    if (s_hi <= s_lo) return i32x4{0, 0, 0, 0};
-    const int8_t *p = img + (static_cast<int64_t>(ih) * cv.W + iw0 + s_lo) * cv.C;
-    return shift_up_bytes(load16_masked(p, (s_hi - s_lo) * cv.C), s_lo * cv.C);
+    const int lo = j16 > s_lo * cv.C ? j16 : s_lo * cv.C;
+    int hi = j16 + 16 < cv.run ? j16 + 16 : cv.run;
+    hi = hi < s_hi * cv.C ? hi : s_hi * cv.C;
+    if (hi <= lo) return i32x4{0, 0, 0, 0};
+    const int8_t *p = img + (static_cast<int64_t>(ih) * cv.W + iw0) * cv.C + lo;
+    return shift_up_bytes(load16_masked(p, hi - lo), lo - j16);
 }
 
 // SRC 0: the product of the operands described by g.  SRC 1: implicit-GEMM
@@ -256,9 +262,13 @@ __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &
                     const int col = n0 + r;
                     const int kk = k0 + 16 * c;
                     if (SRC == 1 && cv.run) {
-                        // run form: filter row kk / 16 of output channel col
-                        const int8_t *p = g.B + static_cast<int64_t>(col) * g.ldb + (kk >> 4) * cv.run;
-                        rb[i] = load16_masked(p, col < g.N && kk < g.K ? cv.run : 0);
+                        // run form: piece j of filter row r of output channel col
+                        const int pi = kk >> 4;
+                        const int r = fast_div(pi, cv.runp_div);
+                        const int j16 = 16 * (pi - r * cv.runp);
+                        const int8_t *p = g.B + static_cast<int64_t>(col) * g.ldb + r * cv.run + j16;
+                        const int nb = cv.run - j16 < 16 ? cv.run - j16 : 16;
+                        rb[i] = load16_masked(p, col < g.N && kk < g.K ? nb : 0);
                     } else {
                         const int8_t *p = g.B + static_cast<int64_t>(col) * g.ldb + kk;
                         rb[i] = FAST ? load16(p) : load16_masked(p, col < g.N ? clamp16(g.K - kk) : 0);
