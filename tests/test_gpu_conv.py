@@ -85,13 +85,19 @@ def test_selected_config_shapes(t):
     check(t, (4, 1, 1, 16, 8, 3, 3), (1, 1))
 
 
-ODD = [  # channel counts that are not multiples of 16: the byte-gather form
+ODD = [  # channel counts that are not multiples of 16: the gather form
     ((2, 9, 11, 3, 24, 3, 3), (1, 1), (1, 1), (1, 1)),
     ((1, 13, 7, 1, 70, 3, 3), (0, 2), (2, 1), (1, 1)),
     ((3, 8, 8, 24, 17, 1, 1), (0, 0), (1, 1), (1, 1)),
     ((1, 17, 15, 5, 130, 5, 3), (2, 1), (1, 2), (2, 1)),
     ((2, 6, 6, 17, 9, 7, 7), (3, 3), (1, 1), (1, 1)),
     ((1, 12, 12, 8, 33, 3, 3), (1, 1), (3, 3), (2, 2)),
+    # run form: filter rows of several 16-byte pieces, pieces that split a
+    # tap's channels, padding wider than the image border, stride 2
+    ((2, 15, 13, 3, 40, 7, 7), (3, 3), (2, 2), (1, 1)),
+    ((1, 9, 10, 63, 20, 3, 3), (1, 1), (1, 1), (2, 1)),
+    ((2, 5, 6, 7, 12, 5, 5), (4, 4), (1, 1), (1, 1)),
+    ((1, 4, 21, 11, 8, 1, 9), (0, 4), (1, 3), (1, 1)),
 ]
 
 
