@@ -205,8 +205,9 @@ int tile_config_split_k(int config_id, int M, int N, int K, int num_cu);
  * of 16 and x and w 16-byte aligned, every 16-byte chunk of the lowered
  * matrix is 16 channels of one tap and goes to LDS by DMA; otherwise (the
  * first layer of a network, C = 3: reduction 27 for 3 x 3 filters) the rows
- * are gathered byte by byte into registers, a slower form with the same
- * result.  Errors, all found on the host before anything is enqueued:
+ * are gathered into registers, a slower form with the same result: with
+ * dil_w = 1 a filter row's S*C bytes lie contiguously in the image and are
+ * read in 16-byte pieces, else byte by byte.  Errors, all found on the host before anything is enqueued:
  * TDI8_ERR_INVALID_VALUE (a size, y's alignment, or N*P*Q or R*S*C above
  * INT_MAX),
  * TDI8_ERR_NULL_POINTER, TDI8_ERR_ALIASING (y overlaps x or w),

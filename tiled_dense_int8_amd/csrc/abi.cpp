@@ -302,7 +302,7 @@ int conv_entry(int cfg, const ConvShape &c, const int8_t *x, const int8_t *w, in
     g.tiles_m = static_cast<int>(tm);
     g.tiles_n = static_cast<int>(tn);
     // 16-byte DMA chunks are 16 channels of one tap: C a multiple of 16 and
-    // 16-byte aligned operands; otherwise the byte-gather form.
+    // 16-byte aligned operands; otherwise the gather form.
     const bool dma = c.C % 16 == 0 && aligned(x, 16) && aligned(w, 16);
     cv.tile_in_tap = dma && c.C % sc.bk == 0;
     // gather form without horizontal dilation: the run form (conv_run16),

@@ -27,7 +27,7 @@ struct KernelSet {
     const void *split[2];
     const void *edge[2];
     const void *conv;   // implicit-GEMM convolution form (null for the skinny family)
-    const void *conv_gather;  // its byte-gather form: any channel count or alignment
+    const void *conv_gather;  // its gather form: any channel count or alignment
     const void *rr_group;  // row-major B column-group form (skinny family only)
 };
 

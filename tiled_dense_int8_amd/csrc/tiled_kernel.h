@@ -417,8 +417,9 @@ __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(GemmArgs g) {
 }
 
 // Implicit-GEMM convolution for any channel count and alignment: the
-// predicated kernel with A gathered byte by byte (the DMA form needs 16-byte
-// chunks of 16 channels).
+// predicated kernel with A gathered into registers, in 16-byte pieces of
+// filter-row runs (conv_run16, dw = 1) or byte by byte (conv_gather16); the
+// DMA form needs 16-byte chunks of 16 channels.
 template <int MF, int WM, int WN, int MT, int NT, int BK>
 __global__ void __launch_bounds__(WM * WN * 64) conv_gather_kernel(GemmArgs g, ConvParams cv) {
     tiled_body<MF, WM, WN, MT, NT, BK, true, false, 1>(g, cv);
