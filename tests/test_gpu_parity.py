@@ -153,11 +153,13 @@ def test_split_k_deterministic(lib):
 
 
 def test_skinny_row_major_column_groups(lib):
-    """Row-major B on a skinny configuration: when 128-column groups and the
-    K slices (K tile 512 for 16-row tiles, 256 for 32-row ones) divide the
-    problem, a block covers 128 columns over 1/G of K (G = 128 / block width)
-    and adds into a zeroed C; otherwise the per-tile form runs.  Both must
-    equal the oracle, and the ldc padding must survive the zeroing."""
+    """Row-major B on a skinny configuration: when 128-column groups divide N
+    and the G K slices are whole 16-byte chunks (K a multiple of 16 G), a
+    block covers 128 columns over 1/G of K (G = 128 / block width; a slice
+    may end inside a K tile) and adds into a zeroed C; otherwise the per-tile
+    form runs (K a multiple of 16 that is not one of the chunk: a partial last
+    chunk).  Both must equal the oracle, and the ldc padding must survive the
+    zeroing."""
     t = lib
     for c in table(t):
         if c.family != 1:
@@ -165,7 +167,10 @@ def test_skinny_row_major_column_groups(lib):
         G = 128 // c.block_n
         kt = G * (512 if c.block_m == 16 else 256)
         for (M, N, K, ldc_pad) in [(c.block_m, 128, kt, 0), (2 * c.block_m, 384, 2 * kt, 8),
-                                   (c.block_m, 256, 3 * kt, 4), (c.block_m, 128, kt + c.block_k, 0)]:
+                                   (c.block_m, 256, 3 * kt, 4), (c.block_m, 128, kt + c.block_k, 0),
+                                   (c.block_m, 128, 16 * G * 5, 0), (c.block_m - 3, 256, 16 * G * 37, 4),
+                                   (c.block_m, 128 + c.block_n, 16 * G * 37, 0),
+                                   (c.block_m, 128 + c.block_n, 1000, 0)]:
             A, B = synthetic.gemm_inputs(M, N, K, seed=M + N + K + c.id)
             check_case(DeviceCase(A, B, False, ldc=N + ldc_pad), f"rr groups cfg{c.id}", config=c.id)
 

@@ -179,12 +179,15 @@ int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, cons
                                 block, stream);
     } else {
         // the unpredicated forms move B by 16-byte LDS DMA loads in both
-        // layouts; a ragged M (M < 16 included) reads zero chunks past M
-        fast = N % c.bn == 0 && K % c.bk == 0 && a_ok && aligned(B, 16) && ldb % 16 == 0 && c_ok;
+        // layouts; a ragged M (M < 16 included) reads zero chunks past M, and
+        // a last, partial K chunk zero pieces past K (K a multiple of 16)
+        const bool dma_ok = a_ok && aligned(B, 16) && ldb % 16 == 0 && c_ok;
+        fast = N % c.bn == 0 && K % 16 == 0 && dma_ok;
         // Row-major B: the column-group form (kernel_table.h) when its
-        // 128-column groups and K slices divide the problem.
+        // 128-column groups divide N and its G K slices are whole 16-byte
+        // chunks (a slice may end inside a K tile: the edge form).
         const int groups = kRrGroupCols / c.bn;
-        if (!bcol && fast && N % kRrGroupCols == 0 && K % (groups * rr_group_bk(c.bm)) == 0) {
+        if (!bcol && dma_ok && N % kRrGroupCols == 0 && K % (groups * 16) == 0) {
             const int64_t tm = (M + static_cast<int64_t>(c.bm) - 1) / c.bm;
             const int64_t tn = N / kRrGroupCols;
             if (tm * tn * groups <= INT_MAX / 512) {

@@ -179,17 +179,20 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
     const int grp = lane >> 4;
     const int m0 = blockIdx.y * BM;
     const int n0 = blockIdx.x * BN;
-    const int nch = g.K / KC;
+    const int nch = (g.K + KC - 1) / KC;
 
-    // A rows past M (a ragged M, e.g. M < 16) read the zero chunk (ok false).
+    // A rows past M (a ragged M, e.g. M < 16) read the zero chunk (ok false),
+    // and so do the 16-byte pieces at or past K of a last, partial chunk (K a
+    // multiple of 16; kin: the piece's K offset within a chunk).
     const int8_t *src[LPW];
-    int dst_off[LPW];
+    int dst_off[LPW], kin[LPW];
     bool ok[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int x = i * WK + wave;
         const int row = x / PIECES;
         const int piece = x % PIECES;
+        kin[i] = piece * 1024 + 16 * lane;
         ok[i] = row >= BM || m0 + row < g.M;
         src[i] = (row < BM ? g.A + static_cast<int64_t>(ok[i] ? m0 + row : m0) * g.lda
                            : g.B + static_cast<int64_t>(n0 + row - BM) * g.ldb) + piece * 1024 + 16 * lane;
@@ -202,7 +205,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
     auto issue = [&](int c) {
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
-            const int8_t *p = ok[i] ? src[i] + c * KC : zero_chunk;
+            const int8_t *p = ok[i] && c * KC + kin[i] < g.K ? src[i] + c * KC : zero_chunk;
             if (b_once && (i * WK + wave) / PIECES >= BM)
                 __builtin_amdgcn_global_load_lds(p, (lds_void_t *)(buf[c & 1] + dst_off[i]), 16, 0, kLoadStream);
             else
@@ -316,12 +319,12 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
     const int cb = (nb & 7) == 0 ? (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3) : blockIdx.x;
     const int m0 = blockIdx.y * BM;
     const int n0 = cb * BN;
-    const int nch = g.K / KC;
+    const int nch = (g.K + KC - 1) / KC;  // a last, partial chunk reads zero pieces past K
 
     // K row of this lane's piece within a 64-row group (inverse of the slot map)
     const int krow = (lane & 7) + 8 * (lane >> 5) + 16 * ((lane >> 3) & 3);
     const int8_t *src[LPW];
-    int dst_off[LPW];
+    int dst_off[LPW], kin[LPW];  // kin: the slot's K offset within a chunk
     bool is_b[LPW], ok[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -330,6 +333,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
         if (x < A_LOADS) {
             const int row = x / PIECES;
             const int piece = x % PIECES;
+            kin[i] = piece * 1024 + 16 * lane;
             ok[i] = m0 + row < g.M;   // A rows past M read the zero chunk
             src[i] = g.A + static_cast<int64_t>(ok[i] ? m0 + row : m0) * g.lda + piece * 1024 + 16 * lane;
             dst_off[i] = row * RS + piece * 1024;
@@ -338,6 +342,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
             const int xb = x - A_LOADS;
             const int j = xb / GROUPS;
             const int grp64 = xb % GROUPS;
+            kin[i] = 64 * grp64 + krow;
             src[i] = g.B + static_cast<int64_t>(64 * grp64 + krow) * g.ldb + n0 + 16 * j;
             dst_off[i] = A_REGION + j * KC * 16 + grp64 * 1024;
             is_b[i] = true;
@@ -347,7 +352,8 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const int64_t off = is_b[i] ? static_cast<int64_t>(c) * KC * g.ldb : static_cast<int64_t>(c) * KC;
-            __builtin_amdgcn_global_load_lds(ok[i] ? src[i] + off : zero_chunk, (lds_void_t *)(buf[c & 1] + dst_off[i]),
+            const bool in = ok[i] && c * KC + kin[i] < g.K;
+            __builtin_amdgcn_global_load_lds(in ? src[i] + off : zero_chunk, (lds_void_t *)(buf[c & 1] + dst_off[i]),
                                              16, 0, 0);
         }
     };
