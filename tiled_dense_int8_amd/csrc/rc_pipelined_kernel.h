@@ -480,7 +480,7 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
             for (int idx = threadIdx.x; idx < rows * BN; idx += NW * 64) {
                 const int r = idx / BN;
                 const int c = idx - r * BN;
-                if (!EDGE || m0 + p0 + r < g.M)
+                if (!EDGE || (m0 + p0 + r < g.M && n0 + c < g.N))
                     atomicAdd(g.C + static_cast<int64_t>(m0 + p0 + r) * g.ldc + n0 + c, cl[r * RS + c]);
             }
         }
