@@ -175,10 +175,10 @@ int select_tile_config_for(int M, int N, int K, const tdi8_hw_info *hw,
  * needs no device.  Returns >= 1 or a negative tdi8_status.
  *
  * A skinny configuration with row-major B (gemm_s8s8s32), 16-byte aligned
- * operands, N a multiple of 16 and K a multiple of 16 G, G = 128 / block
- * width, also enqueues two kernels: each block covers 128 columns (the last
- * ones may end at N) over 1/G of K (whole 128-byte lines of every B row it
- * reads), adding into the zeroed C window.  Its K split is
+ * operands, N and K multiples of 16, also enqueues two kernels: each block
+ * covers 128 columns (the last ones may end at N) over one of G = 128 /
+ * block width slices of K (whole 128-byte lines of every B row it reads),
+ * adding into the zeroed C window.  Its K split is
  * a property of the row-major form and is not what this function reports. */
 int tile_config_split_k(int config_id, int M, int N, int K, int num_cu);
 

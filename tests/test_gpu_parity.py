@@ -153,13 +153,12 @@ def test_split_k_deterministic(lib):
 
 
 def test_skinny_row_major_column_groups(lib):
-    """Row-major B on a skinny configuration: when 128-column groups divide N
-    and the G K slices are whole 16-byte chunks (K a multiple of 16 G), a
-    block covers 128 columns over 1/G of K (G = 128 / block width; a slice
-    may end inside a K tile) and adds into a zeroed C; otherwise the per-tile
-    form runs (K a multiple of 16 that is not one of the chunk: a partial last
-    chunk).  Both must equal the oracle, and the ldc padding must survive the
-    zeroing."""
+    """Row-major B on a skinny configuration: with N and K multiples of 16 a
+    block covers 128 columns (the last group may end at N) over one of G =
+    128 / block width K slices of ceil(K / 16 / G) chunks (the last ones
+    shorter or empty; a slice may end inside a K tile) and adds into a zeroed
+    C; otherwise the predicated form runs.  Both must equal the oracle, and
+    the ldc padding must survive the zeroing."""
     t = lib
     for c in table(t):
         if c.family != 1:
@@ -170,7 +169,10 @@ def test_skinny_row_major_column_groups(lib):
                                    (c.block_m, 256, 3 * kt, 4), (c.block_m, 128, kt + c.block_k, 0),
                                    (c.block_m, 128, 16 * G * 5, 0), (c.block_m - 3, 256, 16 * G * 37, 4),
                                    (c.block_m, 128 + c.block_n, 16 * G * 37, 0),
-                                   (c.block_m, 128 + c.block_n, 1000, 0)]:
+                                   (c.block_m, 128 + c.block_n, 1000, 0),
+                                   # K slices of unequal length, and empty ones
+                                   (c.block_m, 256, 16 * G * 5 + 48, 0), (c.block_m, 128, 16, 0),
+                                   (2 * c.block_m - 1, 384, 4000, 8)]:
             A, B = synthetic.gemm_inputs(M, N, K, seed=M + N + K + c.id)
             check_case(DeviceCase(A, B, False, ldc=N + ldc_pad), f"rr groups cfg{c.id}", config=c.id)
 

@@ -183,11 +183,12 @@ int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, cons
         // a last, partial K chunk zero pieces past K (K a multiple of 16)
         const bool dma_ok = a_ok && aligned(B, 16) && ldb % 16 == 0 && c_ok;
         fast = N % c.bn == 0 && K % 16 == 0 && dma_ok;
-        // Row-major B: the column-group form (kernel_table.h) when N is whole
-        // 16-byte chunks and its G K slices are too (the edge form: a last
-        // group may end inside its 128 columns, a slice inside a K tile).
+        // Row-major B: the column-group form (kernel_table.h) when N and K
+        // are whole 16-byte chunks (the edge form: a last group may end
+        // inside its 128 columns, a K slice inside a K tile; the last slices
+        // may be shorter).
         const int groups = kRrGroupCols / c.bn;
-        if (!bcol && dma_ok && N % 16 == 0 && K % (groups * 16) == 0) {
+        if (!bcol && dma_ok && N % 16 == 0 && K % 16 == 0) {
             const int64_t tm = (M + static_cast<int64_t>(c.bm) - 1) / c.bm;
             const int64_t tn = (N + kRrGroupCols - 1) / kRrGroupCols;
             if (tm * tn * groups <= INT_MAX / 512) {

@@ -130,8 +130,17 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
         const int tiles = g.tiles_m * g.tiles_n;
         const int slice = bid / tiles;
         bid -= slice * tiles;
-        kslice = g.K / g.splits;
-        k_begin = static_cast<int64_t>(slice) * kslice;
+        if constexpr (EDGE) {
+            // K a multiple of 16: slices of ceil(K / 16 / splits) chunks, the
+            // last ones shorter or empty
+            const int nominal = 16 * ((g.K / 16 + g.splits - 1) / g.splits);
+            k_begin = static_cast<int64_t>(slice) * nominal;
+            kslice = g.K - k_begin < nominal ? static_cast<int>(g.K - k_begin) : nominal;
+            if (kslice < 0) kslice = 0;
+        } else {
+            kslice = g.K / g.splits;
+            k_begin = static_cast<int64_t>(slice) * kslice;
+        }
     }
     int tm, tn;
     tile_of_block(g, bid, tm, tn);
