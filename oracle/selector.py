@@ -45,7 +45,8 @@ Readings:
       height BM >= m (else, when n <= skinny_max_m, the smallest block width
       BN >= n: a skinny block streams the large operand once whichever side
       is small); those reaching Thread_Blocks >= num_cu are kept (all if
-      none), then steps 4 and 5 as below.
+      none) and of these the smallest block width BN (block height BM on
+      the n route), then steps 4 and 5 as below.
   claim 5: the compute-to-memory ratio of a BM x BN tile over a K-tile of
       depth BK is BM*BN*BK / (BM*BK + BK*BN) = BM*BN / (BM + BN) (the B tile's
       width is read with n_tiles).  Step 4 keeps every configuration tied at
@@ -225,6 +226,10 @@ def select(m: int, n: int, k: int, hw: Hw, table: list[Cfg]) -> Result:
                 route = 2
                 fill = [c for c in skinny if thread_blocks(c, m, n) >= hw.num_cu]
                 s3 = fill if fill else skinny
+                # of those, the smallest extent along the other dimension
+                other = (lambda c: c.BN) if m <= hw.skinny_max_m else (lambda c: c.BM)
+                least = min(other(c) for c in s3)
+                s3 = [c for c in s3 if other(c) == least]
     trace["step3"] = [c.id for c in s3]
     trace["route"] = route
     pick = _steps_4_5(s3, m, n, hw, trace)

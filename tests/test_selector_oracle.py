@@ -49,21 +49,21 @@ def test_derived_quantities():
     (256, 256, 2, 1),
     # 16 x 4096: fallback, m <= 32 -> skinny with BM = 16: id6 has 256 blocks >= 256, id7 128 < 256 -> id6
     (16, 4096, 6, 2),
-    # 16 x 8192: id6 512 and id7 256 both fill; ratio 16*32/48 > 16*16/32 -> id7
-    (16, 8192, 7, 2),
+    # 16 x 8192: id6 512 and id7 256 both fill; the smallest block width -> id6
+    (16, 8192, 6, 2),
     # 17 x 4096: smallest skinny BM >= 17 is 32 -> id8 (256 blocks)
     (17, 4096, 8, 2),
     # 33 x 4096: step 1 keeps block heights <= max(33, 32) = 33, i.e. only id5 (32 x 32);
     # 2 * 128 = 256 < 8 * 256 blocks -> fallback; id5 is its own reuse-1 sibling; too tall
     # for the skinny family -> id5
     (33, 4096, 5, 1),
-    # 1 x 1: fallback then skinny; nothing fills, keep {6, 7}; ratio picks id7
-    (1, 1, 7, 2),
+    # 1 x 1: fallback then skinny; nothing fills, keep {6, 7}; the smallest block width -> id6
+    (1, 1, 6, 2),
     # 4096 x 16: M is large, N = 16 small: skinny by block width: smallest BN >= 16 is
     # 16 (id6 16 x 16, id8 32 x 16); id6 256 x 1 = 256 blocks, id8 128 < 256 -> id6
     (4096, 16, 6, 2),
-    # 8192 x 16: id6 512 and id8 256 both fill; ratio 32*16/48 > 16*16/32 -> id8
-    (8192, 16, 8, 2),
+    # 8192 x 16: id6 512 and id8 256 both fill; the smallest block height -> id6
+    (8192, 16, 6, 2),
     # 4096 x 17: smallest BN >= 17 is 32 -> id7 (16 x 32, 256 blocks)
     (4096, 17, 7, 2),
     # 4096 x 33: no skinny width reaches 33 and M > 32: the fallback's pick stands;

@@ -17,7 +17,8 @@
 //          candidates then become the skinny family with the smallest block
 //          height >= M (else, for N <= skinny_max_m, with the smallest block
 //          width >= N), keeping those with at least one block per compute
-//          unit (all of them if none has);
+//          unit (all of them if none has) and of these the smallest block
+//          width (block height);
 //  step 4  keep the largest compute-to-memory ratio of a K step,
 //          BM*BN*BK / (BM*BK + BK*BN) = BM*BN / (BM + BN), compared exactly
 //          by cross-multiplication (claim 5; the B tile width uses n_tiles);
@@ -185,7 +186,16 @@ int select_config(int M, int N, int K, const tdi8_hw_info &hw, const int *bpc, t
                     if (thread_blocks(sk[i].c, M, N) >= hw.num_cu) list[nfill++] = sk[i];
                 if (nfill == 0)
                     for (int i = 0; i < nsk; ++i) list[nfill++] = sk[i];
-                n3 = nfill;
+                // of those, the smallest extent along the other dimension:
+                // the most blocks, each streaming its share of the large
+                // operand
+                auto other = [&](const StaticCfg &c) { return by_m ? c.bn : c.bm; };
+                int least = 0;
+                for (int i = 0; i < nfill; ++i)
+                    if (least == 0 || other(list[i].c) < least) least = other(list[i].c);
+                n3 = 0;
+                for (int i = 0; i < nfill; ++i)
+                    if (other(list[i].c) == least) list[n3++] = list[i];
             }
         }
     }
