@@ -103,7 +103,9 @@ int gemm_s8s8s32_with_config(int config_id, int b_col_major, int M, int N, int K
  * register-limited active threads per compute unit reach the threshold;
  * keep those launching at least (compute units x resident blocks per compute
  * unit) blocks, or, if none does, every configuration reduced to reuse 1
- * (then, for M <= 32 or else N <= 32, the skinny family); keep the largest compute-to-memory
+ * (then, for M <= 32 or else N <= 32, the skinny family: the smallest block
+ * height >= M, or width >= N, then the smallest extent along the other side
+ * among those launching a block per compute unit); keep the largest compute-to-memory
  * ratio BM*BN/(BM+BN); keep the fewest rounds of resident blocks; first in
  * table order.  Host only; pure after the first call's initialisation. */
 int select_tile_config(int M, int N, int K);
@@ -175,7 +177,8 @@ int select_tile_config_for(int M, int N, int K, const tdi8_hw_info *hw,
  * needs no device.  Returns >= 1 or a negative tdi8_status.
  *
  * A skinny configuration with row-major B (gemm_s8s8s32), 16-byte aligned
- * operands, N and K multiples of 16, also enqueues two kernels: each block
+ * operands, N and K multiples of 16 and N a multiple of 128 or above 256,
+ * also enqueues two kernels: each block
  * covers 128 columns (the last ones may end at N) over one of G = 128 /
  * block width slices of K (whole 128-byte lines of every B row it reads),
  * adding into the zeroed C window.  Its K split is

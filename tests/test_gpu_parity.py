@@ -153,8 +153,9 @@ def test_split_k_deterministic(lib):
 
 
 def test_skinny_row_major_column_groups(lib):
-    """Row-major B on a skinny configuration: with N and K multiples of 16 a
-    block covers 128 columns (the last group may end at N) over one of G =
+    """Row-major B on a skinny configuration: with N and K multiples of 16 and
+    N whole 128-column groups or more than two of them, a block covers 128
+    columns (the last group may end at N) over one of G =
     128 / block width K slices of ceil(K / 16 / G) chunks (the last ones
     shorter or empty; a slice may end inside a K tile) and adds into a zeroed
     C; otherwise the predicated form runs.  Both must equal the oracle, and
@@ -172,7 +173,9 @@ def test_skinny_row_major_column_groups(lib):
                                    (c.block_m, 128 + c.block_n, 1000, 0),
                                    # K slices of unequal length, and empty ones
                                    (c.block_m, 256, 16 * G * 5 + 48, 0), (c.block_m, 128, 16, 0),
-                                   (2 * c.block_m - 1, 384, 4000, 8)]:
+                                   (2 * c.block_m - 1, 384, 4000, 8),
+                                   # a last group that ends inside its 128 columns
+                                   (c.block_m, 400, 16 * G * 5 + 48, 4)]:
             A, B = synthetic.gemm_inputs(M, N, K, seed=M + N + K + c.id)
             check_case(DeviceCase(A, B, False, ldc=N + ldc_pad), f"rr groups cfg{c.id}", config=c.id)
 
