@@ -164,13 +164,16 @@ int select_tile_config_for(int M, int N, int K, const tdi8_hw_info *hw,
 
 /* K slices the gemm entry points use with configuration `config_id` for an
  * M x K by K x N product on a device of `num_cu` compute units, when the
- * operands take the unpredicated path with sizes that are multiples of the
- * block tile (16-byte aligned pointers, lda and ldb multiples of 16, ldc of
- * 4); other operands are never split.  Splitting K with integer atomics is the contest
- * write-up's "Split K" paragraph, added after the five steps of the
- * selection: while the tiles times twice the slices still fit one block per
- * compute unit, and each slice stays a whole number of at least four K
- * tiles, the slices double.  1 = no split (always for the skinny family).
+ * operands take the unpredicated path (16-byte aligned pointers, lda and ldb
+ * multiples of 16, ldc of 4, K a multiple of 16, and with row-major B N
+ * too); other operands are never split.  Splitting K with integer atomics is
+ * the contest write-up's "Split K" paragraph, added after the five steps of
+ * the selection: counting the partial tiles at the ends of M and N, while
+ * the tiles times twice the slices still fit one block per compute unit, and
+ * K over twice the slices is still at least four K tiles, the slices double.
+ * Slices are whole 16-byte chunks of K, differing by at most one; when M, N
+ * and every slice are whole tiles the whole-tile form runs, else the edge
+ * form.  1 = no split (always for the skinny family).
  * A split call enqueues two kernels on the stream: one zeroes the C window,
  * the other adds every slice's partial sums into it; the result is the same
  * bytes as without the split (integer addition in any order).  Host only,

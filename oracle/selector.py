@@ -162,24 +162,21 @@ def _steps_4_5(cands: list[Cfg], m: int, n: int, hw: Hw, trace: dict) -> Cfg:
 
 
 def split_k(c: Cfg, m: int, n: int, k: int, num_cu: int) -> int:
-    """K slices for configuration c when its unpredicated form runs (sizes
-    multiples of the block tile): a CDNA4 addition after the five steps, from
-    the contest write-up's "Split K" paragraph (partial sums over K slices
-    added with integer atomics).  Reading: the slice count s is a power of two,
-    the largest with tiles * s <= num_cu whose slices are each a whole number
-    of at least four K tiles; the skinny family and tile-ragged shapes never
-    split."""
+    """K slices for configuration c when its unpredicated form runs (K a
+    multiple of 16 bytes): a CDNA4 addition after the five steps, from the
+    contest write-up's "Split K" paragraph (partial sums over K slices added
+    with integer atomics).  Reading: the slice count s is a power of two, the
+    largest with tiles * s <= num_cu (tiles counting the partial ones at the
+    ends of M and N) and K / s at least four K tiles (slices are whole 16-byte
+    chunks and need not be whole K tiles); the skinny family never splits."""
     bk = c.block_k
-    if c.family != "general" or m % c.BM or n % c.BN or k % bk or min(m, n, k) <= 0:
+    if c.family != "general" or k % 16 or min(m, n, k) <= 0:
         return 1
-    tiles = (m // c.BM) * (n // c.BN)
+    tiles = -(-m // c.BM) * -(-n // c.BN)
     best = 1
     s = 2
-    while tiles * s <= num_cu:
-        if k % (s * bk) == 0 and k // s >= 4 * bk:
-            best = s
-        else:
-            break
+    while tiles * s <= num_cu and k // s >= 4 * bk:
+        best = s
         s *= 2
     return best
 

@@ -79,6 +79,15 @@ def test_unpredicated_split_form_large_ld(t, bcm):
 
 
 @pytest.mark.parametrize("bcm", [True, False])
+def test_unpredicated_edge_split_form_large_ld(t, bcm):
+    """Ragged M and N over a long K: the K split of the edge form."""
+    num_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    cid = t.select_tile_config(300, 272, 4096)
+    assert t.tile_config_split_k(cid, 300, 272, 4096, num_cu) > 1
+    run_strided(t, "edge split form", 300, 272, 4096, bcm, L23, L23 if bcm else 2 ** 19 + 2 ** 16, L23, seed=16)
+
+
+@pytest.mark.parametrize("bcm", [True, False])
 def test_predicated_form_large_ld(t, bcm):
     """Odd leading dimensions: the predicated kernel."""
     run_strided(t, "predicated form", 300, 272, 300, bcm, L23 + 1, L23 + 3, L23 + 1, seed=13)

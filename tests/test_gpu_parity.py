@@ -156,8 +156,9 @@ def test_skinny_row_major_column_groups(lib):
     """Row-major B on a skinny configuration: with N and K multiples of 16 and
     N whole 128-column groups or more than two of them, a block covers 128
     columns (the last group may end at N) over one of G =
-    128 / block width K slices of ceil(K / 16 / G) chunks (the last ones
-    shorter or empty; a slice may end inside a K tile) and adds into a zeroed
+    128 / block width K slices of whole 16-byte chunks (slices differ by at
+    most one chunk, empty when K / 16 < G; a slice may end inside a K tile)
+    and adds into a zeroed
     C; otherwise the predicated form runs.  Both must equal the oracle, and
     the ldc padding must survive the zeroing."""
     t = lib
@@ -199,10 +200,33 @@ def test_split_k_every_general_config(lib, bcm):
 
 
 @pytest.mark.parametrize("bcm", [True, False])
+def test_split_k_edge_form_every_general_config(lib, bcm):
+    """The K split of the edge form: M and N ending inside a tile (N any
+    width with column-major B), K slices of whole 16-byte chunks that end
+    inside K tiles and differ by one chunk, and whole tiles whose K does not
+    split into whole K tiles.  Bytes must equal the oracle's; C's padding
+    (past a partial group of four columns too) must survive the zeroing."""
+    t = lib
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for c in table(t):
+        if c.family != 0:
+            continue
+        bm, bn, bk = c.block_m, c.block_n, c.block_k
+        nr = bn + (5 if bcm else 16)
+        for (M, N, K, pad) in [(bm + 7, nr, 33 * bk + 16, 0), (bm - 1, nr, 16 * 131, 3),
+                               (bm, bn, 13 * bk, 4), (bm, bn, 9 * bk + 48, 0), (2 * bm + 1, 2 * bn, 8 * bk + 16, 8)]:
+            s = t.tile_config_split_k(c.id, M, N, K, cus)
+            assert s >= 2, (c.id, M, N, K, s)
+            A, B = synthetic.gemm_inputs(M, N, K, seed=M + N + K + c.id)
+            check_case(DeviceCase(A, B, bcm, ldc=N + pad), f"edge split-K x{s} cfg{c.id} {M}x{N}x{K}", config=c.id)
+
+
+@pytest.mark.parametrize("bcm", [True, False])
 def test_split_k_selected_long_k_shapes(lib, bcm):
     t = lib
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for (M, N, K) in [(256, 256, 32768), (1024, 1024, 8192), (128, 256, 65536), (64, 128, 131072)]:
+    for (M, N, K) in [(256, 256, 32768), (1024, 1024, 8192), (128, 256, 65536), (64, 128, 131072),
+                      (500, 496, 16384), (1000, 1008, 8192), (300, 304, 32768 + 16)]:
         cid = t.select_tile_config(M, N, K)
         note(f"[info] {M}x{N}x{K} config {cid} splits {t.tile_config_split_k(cid, M, N, K, cus)}")
         A, B = synthetic.gemm_inputs(M, N, K, seed=11)

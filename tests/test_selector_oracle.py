@@ -121,8 +121,8 @@ def test_deterministic_and_k_independent():
 
 def test_split_k_worked_examples():
     """The K-split rule (a CDNA4 addition after the five steps), worked by hand:
-    slices double while tiles * slices <= #CU and each slice keeps a whole
-    number of at least four K tiles."""
+    slices double while tiles * slices <= #CU (partial tiles counted) and K /
+    slices keeps at least four K tiles; K must be whole 16-byte chunks."""
     from oracle.selector import split_k
     g64x128 = Cfg(10, "general", 32, 32, 2, 4, 1, 1, 128, 512, 3)       # 64 x 128, BK 128
     g256 = Cfg(11, "general", 32, 32, 2, 4, 4, 2, 128, 512, 1)          # 256 x 256
@@ -138,10 +138,19 @@ def test_split_k_worked_examples():
     assert split_k(g64x128, 256, 256, 1024, 256) == 2
     # K = 768: two slices of 384 < 512 -> 1
     assert split_k(g64x128, 256, 256, 768, 256) == 1
-    # K = 1536: 1536 % 256 == 0 and 768 >= 512 -> 2; 1536 % 512 == 0 but 384 < 512 -> stop
+    # K = 1536: 768 >= 512 -> 2; 384 < 512 -> stop
     assert split_k(g64x128, 256, 256, 1536, 256) == 2
-    # tile-ragged M, the skinny family: never split
-    assert split_k(g64x128, 100, 256, 32768, 256) == 1
+    # K = 1664 = 13 K tiles: 832 >= 512 -> 2 (slices of 6.5 K tiles); 416 < 512 -> stop
+    assert split_k(g64x128, 256, 256, 1664, 256) == 2
+    # K = 1040 = 65 chunks of 16: 520 >= 512 -> 2
+    assert split_k(g64x128, 64, 128, 1040, 256) == 2
+    # tile-ragged M = 100: 2 x 2 = 4 tiles (one partial row of tiles); 4 * 64 = 256 <= 256
+    # and 32768 / 64 = 512 >= 512 -> 64
+    assert split_k(g64x128, 100, 256, 32768, 256) == 64
+    # 500 x 500: 8 x 4 = 32 tiles; 32 * 8 = 256 and 16384 / 8 = 2048 >= 512 -> 8
+    assert split_k(g64x128, 500, 500, 16384, 256) == 8
+    # K not whole 16-byte chunks, the skinny family: never split
+    assert split_k(g64x128, 256, 256, 32776, 256) == 1
     assert split_k(sk, 16, 4096, 65536, 256) == 1
     # 120 compute units, 8 tiles: 16 * 8 = 128 > 120 -> 8
     assert split_k(g64x128, 256, 256, 32768, 120) == 8

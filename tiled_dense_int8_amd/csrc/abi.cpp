@@ -16,16 +16,22 @@
 
 namespace tdi8 {
 
-// C[0:M, 0:N] = 0 (C 16-byte aligned, ldc and N multiples of 4): run before a
-// K-split launch, whose blocks add their partial sums into C.
+// C[0:M, 0:N] = 0 (C 16-byte aligned, ldc a multiple of 4; a row's last
+// group of four may be partial): run before a K-split launch, whose blocks
+// add their partial sums into C.
 __global__ void __launch_bounds__(256) zero_c_kernel(GemmArgs g) {
-    const int64_t per_row = g.N / 4;
+    const int64_t per_row = (g.N + 3) / 4;
     const int64_t total = per_row * g.M;
     for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < total;
          q += static_cast<int64_t>(gridDim.x) * 256) {
         const int64_t m = q / per_row;
         const int64_t n = 4 * (q - m * per_row);
-        *reinterpret_cast<i32x4 *>(g.C + m * g.ldc + n) = i32x4{0, 0, 0, 0};
+        int32_t *p = g.C + m * g.ldc + n;
+        if (n + 4 <= g.N) {
+            *reinterpret_cast<i32x4 *>(p) = i32x4{0, 0, 0, 0};
+        } else {
+            for (int j = 0; j < g.N - n; ++j) p[j] = 0;
+        }
     }
 }
 
@@ -129,7 +135,7 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // Zero the C window, then launch a K-split kernel whose blocks (one per tile
 // and K slice) add their partial sums into it.
 int launch_split(const void *kernel, GemmArgs &g, dim3 grid, dim3 block, hipStream_t stream) {
-    const int64_t quads = static_cast<int64_t>(g.M) * (g.N / 4);
+    const int64_t quads = static_cast<int64_t>(g.M) * ((g.N + 3) / 4);
     const unsigned zb = static_cast<unsigned>(quads / 256 + 1 < 2048 ? quads / 256 + 1 : 2048);
     void *args[] = {&g};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&zero_c_kernel), dim3(zb), dim3(256), args, 0,
@@ -169,14 +175,17 @@ int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, cons
         // chunks outside the operands read a zero chunk and stores are
         // masked, so M and N are free and K (and, row-major B, N) need only
         // be multiples of 16 (the edge form: sizes that end inside a tile);
-        // the K split only for whole tiles
+        // the K split runs in the whole-tile form when M, N and every slice
+        // are whole tiles, else in the edge form (slices of 16-byte chunks)
         const bool b_ok = aligned(B, 16) && ldb % 16 == 0;
         fast = K % 16 == 0 && (bcol || N % 16 == 0) && a_ok && b_ok && c_ok;
         edge = fast && (M % c.bm != 0 || N % c.bn != 0 || K % c.bk != 0);
-        if (fast && !edge) g.splits = split_k_for(c, M, N, K, num_cu);
-        if (g.splits > 1)
-            return launch_split(kernels()[id].split[bcol ? 1 : 0], g, dim3(static_cast<unsigned>(tm * tn * g.splits)),
-                                block, stream);
+        if (fast) g.splits = split_k_for(c, M, N, K, num_cu);
+        if (g.splits > 1) {
+            const bool whole = !edge && K % (g.splits * c.bk) == 0;
+            const void *k = whole ? kernels()[id].split[bcol ? 1 : 0] : kernels()[id].split_edge[bcol ? 1 : 0];
+            return launch_split(k, g, dim3(static_cast<unsigned>(tm * tn * g.splits)), block, stream);
+        }
     } else {
         // the unpredicated forms move B by 16-byte LDS DMA loads in both
         // layouts; a ragged M (M < 16 included) reads zero chunks past M, and
@@ -439,9 +448,7 @@ int conv2d_select_config(int N, int H, int W, int C, int K, int R, int S, int pa
 int tile_config_split_k(int config_id, int M, int N, int K, int num_cu) {
     if (config_id < 0 || config_id >= TDI8_NUM_CONFIGS) return TDI8_ERR_BAD_CONFIG;
     if (M < 0 || N < 0 || K < 0 || num_cu <= 0) return TDI8_ERR_INVALID_VALUE;
-    const StaticCfg c = static_cfg(config_id);
-    if (c.family != 0 || M % c.bm != 0 || N % c.bn != 0 || K % c.bk != 0) return 1;
-    return split_k_for(c, M, N, K, num_cu);
+    return split_k_for(static_cfg(config_id), M, N, K, num_cu);
 }
 
 int tile_config_info(int id, tdi8_tile_config *out) {

@@ -66,6 +66,17 @@ static const void *edge_entry() {
         return nullptr;
 }
 
+// Its K-split form (slices of 16-byte chunks).
+template <class P, bool BCOL>
+static const void *split_edge_entry() {
+    if constexpr (P::family == 0)
+        return reinterpret_cast<const void *>(
+            &gemm_rc_pipelined_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, stages_for<P, BCOL>(), !BCOL, true,
+                                      true>);
+    else
+        return nullptr;
+}
+
 template <class P>
 static const void *conv_entry() {
     if constexpr (P::family == 0)
@@ -109,6 +120,8 @@ void TDI8_CAT(register_cfg_, TDI8_CFG)(KernelSet *ks) {
     ks->split[1] = split_entry<P, true>();
     ks->edge[0] = edge_entry<P, false>();
     ks->edge[1] = edge_entry<P, true>();
+    ks->split_edge[0] = split_edge_entry<P, false>();
+    ks->split_edge[1] = split_edge_entry<P, true>();
     ks->conv = conv_entry<P>();
     ks->conv_gather = conv_gather_entry<P>();
     ks->rr_group = rr_group_entry<P>();

@@ -19,13 +19,16 @@ TDI8_CONFIG_LIST(TDI8_DEFINE_PARAMS)
 #undef TDI8_DEFINE_PARAMS
 
 // kernel[b_col_major][fast]: host stubs of the four instantiations (the fast
-// general kernel for whole tiles); split[b_col_major]: its K-split form and
-// edge[b_col_major]: its form for sizes that end inside a tile (null for the
-// skinny family); conv: the implicit-GEMM convolution form.
+// general kernel for whole tiles); split[b_col_major]: its K-split form,
+// edge[b_col_major]: its form for sizes that end inside a tile and
+// split_edge[b_col_major]: the K split of that form, whose slices may end
+// inside a K tile (null for the skinny family); conv: the implicit-GEMM
+// convolution form.
 struct KernelSet {
     const void *kernel[2][2];
     const void *split[2];
     const void *edge[2];
+    const void *split_edge[2];
     const void *conv;   // implicit-GEMM convolution form (null for the skinny family)
     const void *conv_gather;  // its gather form: any channel count or alignment
     const void *rr_group;  // row-major B column-group form (skinny family only)

@@ -85,8 +85,9 @@ constexpr int step_group(int ks, int f) {
 }
 
 // SPLIT: the grid holds g.splits blocks per tile, slice s of a tile covering
-// K range [s K / splits, (s + 1) K / splits) and adding its partial sums into
-// C (zeroed beforehand) with integer atomics: exact in any order.
+// K range [s K / splits, (s + 1) K / splits) (with EDGE rounded to 16-byte
+// chunks) and adding its partial sums into C (zeroed beforehand) with integer
+// atomics: exact in any order.
 // EDGE: M, N or K may end inside a tile (chunks outside the operands read the
 // zero chunk, stores are masked); without it M, N and the K extent of a block
 // are whole tiles and the kernel carries none of these tests.
@@ -131,12 +132,12 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
         const int slice = bid / tiles;
         bid -= slice * tiles;
         if constexpr (EDGE) {
-            // K a multiple of 16: slices of ceil(K / 16 / splits) chunks, the
-            // last ones shorter or empty
-            const int nominal = 16 * ((g.K / 16 + g.splits - 1) / g.splits);
-            k_begin = static_cast<int64_t>(slice) * nominal;
-            kslice = g.K - k_begin < nominal ? static_cast<int>(g.K - k_begin) : nominal;
-            if (kslice < 0) kslice = 0;
+            // K a multiple of 16: slice s covers 16-byte chunks [s C / splits,
+            // (s + 1) C / splits) of the C = K / 16, so slices differ by at
+            // most one chunk (empty only when C < splits)
+            const int64_t chunks = g.K / 16;
+            k_begin = 16 * (slice * chunks / g.splits);
+            kslice = static_cast<int>(16 * ((slice + 1) * chunks / g.splits) - k_begin);
         } else {
             kslice = g.K / g.splits;
             k_begin = static_cast<int64_t>(slice) * kslice;

@@ -234,10 +234,10 @@ int select_config(int M, int N, int K, const tdi8_hw_info &hw, const int *bpc, t
 }
 
 int split_k_for(const StaticCfg &c, int M, int N, int K, int num_cu) {
-    if (c.family != 0 || M <= 0 || N <= 0 || K <= 0) return 1;
+    if (c.family != 0 || M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return 1;
     const int64_t tiles = static_cast<int64_t>((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
     int s = 1;
-    while (tiles * 2 * s <= num_cu && K % (2 * s * c.bk) == 0 && K / (2 * s) >= 4 * c.bk) s *= 2;
+    while (tiles * 2 * s <= num_cu && K / (2 * s) >= 4 * c.bk) s *= 2;
     return s;
 }
 

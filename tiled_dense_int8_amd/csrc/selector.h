@@ -24,9 +24,10 @@ int select_config(int M, int N, int K, const tdi8_hw_info &hw, const int *bpc, t
 
 // K slices for the unpredicated form of a general configuration (a CDNA4
 // addition after the five steps; split K with integer atomics, the contest
-// write-up's "Split K" paragraph): while the tiles times twice the slices
-// still fit one block per compute unit, and each slice stays a whole number
-// of at least four K tiles, the slices double.  1 = no split.
+// write-up's "Split K" paragraph): K a multiple of 16, tiles counted with
+// the partial ones at M's and N's ends; while the tiles times twice the
+// slices still fit one block per compute unit, and K over twice the slices
+// is still at least four K tiles, the slices double.  1 = no split.
 int split_k_for(const StaticCfg &c, int M, int N, int K, int num_cu);
 
 }  // namespace tdi8
