@@ -170,7 +170,7 @@ int select_tile_config_for(int M, int N, int K, const tdi8_hw_info *hw,
  * the contest write-up's "Split K" paragraph, added after the five steps of
  * the selection: counting the partial tiles at the ends of M and N, while
  * the tiles times twice the slices still fit one block per compute unit, and
- * K over twice the slices is still at least four K tiles, the slices double.
+ * K over twice the slices is still at least eight K tiles, the slices double.
  * Slices are whole 16-byte chunks of K, differing by at most one; when M, N
  * and every slice are whole tiles the whole-tile form runs, else the edge
  * form.  1 = no split (always for the skinny family).

@@ -167,7 +167,7 @@ def split_k(c: Cfg, m: int, n: int, k: int, num_cu: int) -> int:
     contest write-up's "Split K" paragraph (partial sums over K slices added
     with integer atomics).  Reading: the slice count s is a power of two, the
     largest with tiles * s <= num_cu (tiles counting the partial ones at the
-    ends of M and N) and K / s at least four K tiles (slices are whole 16-byte
+    ends of M and N) and K / s at least eight K tiles (slices are whole 16-byte
     chunks and need not be whole K tiles); the skinny family never splits."""
     bk = c.block_k
     if c.family != "general" or k % 16 or min(m, n, k) <= 0:
@@ -175,7 +175,7 @@ def split_k(c: Cfg, m: int, n: int, k: int, num_cu: int) -> int:
     tiles = -(-m // c.BM) * -(-n // c.BN)
     best = 1
     s = 2
-    while tiles * s <= num_cu and k // s >= 4 * bk:
+    while tiles * s <= num_cu and k // s >= 8 * bk:
         best = s
         s *= 2
     return best

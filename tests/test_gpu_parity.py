@@ -190,7 +190,7 @@ def test_split_k_every_general_config(lib, bcm):
     for c in table(t):
         if c.family != 0:
             continue
-        for (M, N, K) in [(c.block_m, c.block_n, 32 * c.block_k), (2 * c.block_m, c.block_n, 8 * c.block_k)]:
+        for (M, N, K) in [(c.block_m, c.block_n, 32 * c.block_k), (2 * c.block_m, c.block_n, 16 * c.block_k)]:
             s = t.tile_config_split_k(c.id, M, N, K, cus)
             assert s >= 2, (c.id, M, N, K, s)
             A, B = synthetic.gemm_inputs(M, N, K, seed=M + N + K)
@@ -213,8 +213,8 @@ def test_split_k_edge_form_every_general_config(lib, bcm):
             continue
         bm, bn, bk = c.block_m, c.block_n, c.block_k
         nr = bn + (5 if bcm else 16)
-        for (M, N, K, pad) in [(bm + 7, nr, 33 * bk + 16, 0), (bm - 1, nr, 16 * 131, 3),
-                               (bm, bn, 13 * bk, 4), (bm, bn, 9 * bk + 48, 0), (2 * bm + 1, 2 * bn, 8 * bk + 16, 8)]:
+        for (M, N, K, pad) in [(bm + 7, nr, 33 * bk + 16, 0), (bm - 1, nr, 16 * 271, 3),
+                               (bm, bn, 25 * bk, 4), (bm, bn, 17 * bk + 48, 0), (2 * bm + 1, 2 * bn, 16 * bk + 16, 8)]:
             s = t.tile_config_split_k(c.id, M, N, K, cus)
             assert s >= 2, (c.id, M, N, K, s)
             A, B = synthetic.gemm_inputs(M, N, K, seed=M + N + K + c.id)

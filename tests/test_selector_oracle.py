@@ -122,32 +122,32 @@ def test_deterministic_and_k_independent():
 def test_split_k_worked_examples():
     """The K-split rule (a CDNA4 addition after the five steps), worked by hand:
     slices double while tiles * slices <= #CU (partial tiles counted) and K /
-    slices keeps at least four K tiles; K must be whole 16-byte chunks."""
+    slices keeps at least eight K tiles; K must be whole 16-byte chunks."""
     from oracle.selector import split_k
     g64x128 = Cfg(10, "general", 32, 32, 2, 4, 1, 1, 128, 512, 3)       # 64 x 128, BK 128
     g256 = Cfg(11, "general", 32, 32, 2, 4, 4, 2, 128, 512, 1)          # 256 x 256
     sk = Cfg(12, "skinny", 16, 16, 1, 1, 1, 1, 2048, 1024, 1)
     assert (g64x128.BM, g64x128.BN, g256.BM, g256.BN) == (64, 128, 256, 256)
-    # 256x256x32768: 4*2 = 8 tiles; 8*32 = 256 <= 256 and 32768/32 = 1024 >= 512 -> 32
+    # 256x256x32768: 4*2 = 8 tiles; 8*32 = 256 <= 256 and 32768/32 = 1024 >= 8*128 -> 32
     assert split_k(g64x128, 256, 256, 32768, 256) == 32
     # 1024x1024x8192: 16*8 = 128 tiles; 2 slices fill 256 exactly -> 2
     assert split_k(g64x128, 1024, 1024, 8192, 256) == 2
     # 4096^3 with 256x256: 256 tiles, no room -> 1
     assert split_k(g256, 4096, 4096, 4096, 256) == 1
-    # K = 1024: two slices of 512 = 4 tiles of 128; four slices would be 256 -> 2
-    assert split_k(g64x128, 256, 256, 1024, 256) == 2
-    # K = 768: two slices of 384 < 512 -> 1
-    assert split_k(g64x128, 256, 256, 768, 256) == 1
-    # K = 1536: 768 >= 512 -> 2; 384 < 512 -> stop
-    assert split_k(g64x128, 256, 256, 1536, 256) == 2
-    # K = 1664 = 13 K tiles: 832 >= 512 -> 2 (slices of 6.5 K tiles); 416 < 512 -> stop
-    assert split_k(g64x128, 256, 256, 1664, 256) == 2
-    # K = 1040 = 65 chunks of 16: 520 >= 512 -> 2
-    assert split_k(g64x128, 64, 128, 1040, 256) == 2
-    # tile-ragged M = 100: 2 x 2 = 4 tiles (one partial row of tiles); 4 * 64 = 256 <= 256
-    # and 32768 / 64 = 512 >= 512 -> 64
-    assert split_k(g64x128, 100, 256, 32768, 256) == 64
-    # 500 x 500: 8 x 4 = 32 tiles; 32 * 8 = 256 and 16384 / 8 = 2048 >= 512 -> 8
+    # K = 2048: two slices of 1024 = 8 tiles of 128; four slices would be 512 -> 2
+    assert split_k(g64x128, 256, 256, 2048, 256) == 2
+    # K = 1536: two slices of 768 < 1024 -> 1
+    assert split_k(g64x128, 256, 256, 1536, 256) == 1
+    # K = 3072: 1536 >= 1024 -> 2; 768 < 1024 -> stop
+    assert split_k(g64x128, 256, 256, 3072, 256) == 2
+    # K = 2176 = 17 K tiles: 1088 >= 1024 -> 2 (slices of 8.5 K tiles); 544 < 1024 -> stop
+    assert split_k(g64x128, 256, 256, 2176, 256) == 2
+    # K = 2064 = 129 chunks of 16: 1032 >= 1024 -> 2 (slices of 65 and 64 chunks)
+    assert split_k(g64x128, 64, 128, 2064, 256) == 2
+    # tile-ragged M = 100: 2 x 2 = 4 tiles (one partial row of tiles); 4 * 32 = 128 <= 256
+    # and 32768 / 32 = 1024 >= 1024 -> 32; 32768 / 64 = 512 < 1024 -> stop
+    assert split_k(g64x128, 100, 256, 32768, 256) == 32
+    # 500 x 500: 8 x 4 = 32 tiles; 32 * 8 = 256 and 16384 / 8 = 2048 >= 1024 -> 8
     assert split_k(g64x128, 500, 500, 16384, 256) == 8
     # K not whole 16-byte chunks, the skinny family: never split
     assert split_k(g64x128, 256, 256, 32776, 256) == 1

@@ -237,7 +237,7 @@ int split_k_for(const StaticCfg &c, int M, int N, int K, int num_cu) {
     if (c.family != 0 || M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return 1;
     const int64_t tiles = static_cast<int64_t>((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
     int s = 1;
-    while (tiles * 2 * s <= num_cu && K / (2 * s) >= 4 * c.bk) s *= 2;
+    while (tiles * 2 * s <= num_cu && K / (2 * s) >= 8 * c.bk) s *= 2;
     return s;
 }
 
