@@ -217,8 +217,10 @@ def test_split_k_edge_form_every_general_config(lib, bcm):
                                (bm, bn, 25 * bk, 4), (bm, bn, 17 * bk + 48, 0), (2 * bm + 1, 2 * bn, 16 * bk + 16, 8)]:
             s = t.tile_config_split_k(c.id, M, N, K, cus)
             assert s >= 2, (c.id, M, N, K, s)
+            ldc = N + pad
+            ldc += -ldc % 4   # a multiple of 4, as the unpredicated path needs
             A, B = synthetic.gemm_inputs(M, N, K, seed=M + N + K + c.id)
-            check_case(DeviceCase(A, B, bcm, ldc=N + pad), f"edge split-K x{s} cfg{c.id} {M}x{N}x{K}", config=c.id)
+            check_case(DeviceCase(A, B, bcm, ldc=ldc), f"edge split-K x{s} cfg{c.id} {M}x{N}x{K}", config=c.id)
 
 
 @pytest.mark.parametrize("bcm", [True, False])
