@@ -422,6 +422,130 @@ def selector_report(t):
         torch.cuda.empty_cache()
 
 
+# K sweeps of one forced configuration at fixed M and N: the time per launch
+# against K is a line whose slope is the cost of the K loop per K tile and
+# whose intercept is the fixed part (launch, prologue, C drain).
+SWEEPS = {
+    "square-k": dict(config=0, M=4096, N=4096, bcm=True, Ks=[1024, 2048, 4096, 8192, 16384],
+                     warmup=100, steps=200),
+    "skinny-k": dict(config=12, M=16, N=4096, bcm=True, Ks=[4096, 8192, 16384, 32768, 65536],
+                     warmup=500, steps=1000),
+    "ragged-k": dict(config=7, M=1000, N=3000, bcm=True, Ks=[777, 1553, 3105, 6209],
+                     warmup=300, steps=500),
+}
+
+
+def fit_line(xs, ys):
+    """Least-squares slope and intercept of ys against xs."""
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    slope = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sxx
+    return slope, my - slope * mx
+
+
+def k_sweep(t, name, plan_path=None):
+    """Time configuration SWEEPS[name]["config"] (forced) at each K of the
+    sweep, inputs rotating past the caches; print a markdown table with the
+    least-squares line through the event-timed means.  The launch order is
+    written to plan_path (JSON) so that a kernel trace of the same run can be
+    cut into the same segments (--trace-summary)."""
+    import torch
+    sw = SWEEPS[name]
+    info = t.tile_config_info(sw["config"])
+    M, N, bcm = sw["M"], sw["N"], sw["bcm"]
+    sh = torch.cuda.current_stream().cuda_stream
+    plan, rows = [], []
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    for K in sw["Ks"]:
+        w = dict(M=M, N=N, K=K, bcm=bcm)
+        nsets = rotation_sets(w)
+        sets = [(torch.randint(-128, 128, (M, K), dtype=torch.int8, device="cuda", generator=gen),
+                 torch.randint(-128, 128, (N, K) if bcm else (K, N), dtype=torch.int8, device="cuda",
+                               generator=gen),
+                 torch.empty((M, N), dtype=torch.int32, device="cuda")) for _ in range(nsets)]
+        args = [(sw["config"], int(bcm), M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0),
+                 c.data_ptr(), c.stride(0), sh) for (a, b, c) in sets]
+        for i in range(sw["warmup"]):
+            st = t.gemm_s8s8s32_with_config(*args[i % nsets])
+            assert st == t.OK, t.tdi8_status_string(st)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(sw["steps"]):
+            t.gemm_s8s8s32_with_config(*args[i % nsets])
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / sw["steps"]
+        plan += [{"K": K, "phase": "warmup", "launches": sw["warmup"]},
+                 {"K": K, "phase": "timed", "launches": sw["steps"]}]
+        rows.append((K, us))
+        log(f"[sweep] {name} K={K}: {us:.2f} us per launch (events, {nsets} rotating sets)")
+        del sets
+        torch.cuda.empty_cache()
+    if plan_path:
+        with open(plan_path, "w") as f:
+            json.dump({"sweep": name, "config": sw["config"], "M": M, "N": N, "bcm": bcm,
+                       "block_k": info.block_k, "segments": plan}, f, indent=1)
+    print_sweep_table(name, sw, info, rows, "HIP events over the timed launches, back to back (gaps included)")
+
+
+def print_sweep_table(name, sw, info, rows, how):
+    M, N = sw["M"], sw["N"]
+    ks = [k for k, _ in rows]
+    us = [u for _, u in rows]
+    slope, icpt = fit_line(ks, us)
+    bk = info.block_k
+    print(f"| {name}: M={M} N={N}, B {'column' if sw['bcm'] else 'row'}-major, config {sw['config']} "
+          f"({info.block_m}x{info.block_n}x{bk}) | µs per launch | TOPS | algorithmic GB/s | line fit µs |")
+    print("|---|---|---|---|---|")
+    for K, u in rows:
+        byts = M * K + K * N + 4 * M * N
+        print(f"| K={K} | {u:.2f} | {2.0 * M * N * K / (u * 1e-6) / 1e12:.1f} | {byts / (u * 1e-6) / 1e9:.0f} | "
+              f"{icpt + slope * K:.2f} |")
+    print()
+    print(f"Timing: {how}.  Line: {slope * bk:.4f} µs per K tile of {bk} ({slope * 1e3:.4f} ns per unit of K), "
+          f"intercept {icpt:.2f} µs; the K stream alone moves {(M + N) * 1e-3 / slope:.0f} GB/s "
+          f"((M + N) bytes per unit of K over the slope).")
+
+
+def trace_summary(trace_csv, plan_path):
+    """Cut a rocprofv3 kernel trace (CSV) of a --sweep run into the sweep's
+    segments (dispatches of the GEMM kernels in launch order) and print the
+    per-K mean, median, min and p90 kernel durations and the line through the
+    means."""
+    import csv
+    plan = json.load(open(plan_path))
+    recs = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name", "")
+            if "gemm_" in name and "zero_c" not in name:
+                recs.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), name))
+    recs.sort()
+    need = sum(s["launches"] for s in plan["segments"])
+    assert len(recs) == need, f"trace holds {len(recs)} GEMM dispatches, the plan {need}"
+    import tiled_dense_int8_amd as t
+    info = t.tile_config_info(plan["config"])
+    rows, pos, kname = [], 0, recs[0][2]
+    for s in plan["segments"]:
+        seg = recs[pos:pos + s["launches"]]
+        pos += s["launches"]
+        if s["phase"] != "timed":
+            continue
+        d = sorted((e - b) * 1e-3 for b, e, _ in seg)
+        mean = sum(d) / len(d)
+        log(f"[trace] K={s['K']}: mean {mean:.3f} median {d[len(d) // 2]:.3f} min {d[0]:.3f} "
+            f"p90 {d[int(0.9 * (len(d) - 1))]:.3f} us over {len(d)} dispatches")
+        rows.append((s["K"], mean))
+    sw = dict(SWEEPS[plan["sweep"]])
+    print(f"Kernel: `{kname}`")
+    print()
+    print_sweep_table(plan["sweep"], sw, info, rows, "rocprofv3 kernel-trace durations, mean of the timed dispatches")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -436,7 +560,16 @@ def main():
                     help="only time every compiled configuration on a shape suite and print the selector's regret")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (10 times) for counter calibration")
+    ap.add_argument("--sweep", choices=sorted(SWEEPS),
+                    help="only time one forced configuration over a range of K and fit time = a + b K")
+    ap.add_argument("--plan", default=None, help="with --sweep: write the launch plan here (JSON); "
+                    "with --trace-summary: read it")
+    ap.add_argument("--trace-summary", default=None, metavar="CSV",
+                    help="only summarise a rocprofv3 kernel trace of a --sweep run (needs --plan)")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.plan)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -459,6 +592,9 @@ def main():
     torch.cuda.set_device(0)
     if args.selector_report:
         selector_report(t)
+        return
+    if args.sweep:
+        k_sweep(t, args.sweep, args.plan)
         return
     if args.workload in CONV_WORKLOADS:
         print(json.dumps(conv_bench(t, args.workload, args.steps, args.warmup)), flush=True)
