@@ -83,14 +83,26 @@ int gemm_s8s8s32(int M, int N, int K, const int8_t *A, int lda, const int8_t *B,
                  int32_t *C, int ldc, hipStream_t stream);
 
 /* Same as gemm_s8s8s32 with B column-major: B(k,j) at B[j*ldb + k], ldb >= K
- * (B stored N x K with K contiguous, as inference weights usually are). */
+ * (B stored N x K with K contiguous, as inference weights usually are).  This
+ * is the operand order of a convolution lowered to a matrix product in the
+ * contest write-up ("先导杯比赛回顾", 卷积转化 and 多批次展开的 Im2col 方法):
+ * the filter bank, one row of reduction values per output channel, is the
+ * right-hand operand with the reduction dimension contiguous, the layout
+ * that write-up transposes its NCHW data into (NCHW布局空间连续性不佳,
+ * NCHW_2_NHWC) so that the dimension summed over lies contiguously. */
 int gemm_s8s8s32_bt(int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
                     int32_t *C, int ldc, hipStream_t stream);
 
 /* Same product computed with a given configuration id instead of the
- * selected one (b_col_major selects the B layout).  Any general
+ * selected one (b_col_major selects the B layout).  Patent application
+ * CN114238853A, claim 7: the system compiles one kernel per tiling
+ * configuration, the configuration's parameters being the kernel's template
+ * parameters, and runs the one the selection picks; this entry point runs a
+ * compiled configuration by its id, bypassing the selection.  Any general
  * configuration runs any shape; a skinny configuration needs M <= its block
- * height times 65535 (TDI8_ERR_BAD_CONFIG otherwise).  For tests and the
+ * height times 65535 (TDI8_ERR_BAD_CONFIG otherwise).  Arguments, layouts,
+ * ownership and errors as for gemm_s8s8s32; config_id outside
+ * 0 .. tile_config_count()-1 gives TDI8_ERR_BAD_CONFIG.  For tests and the
  * bench, which sweep every compiled configuration. */
 int gemm_s8s8s32_with_config(int config_id, int b_col_major, int M, int N, int K,
                              const int8_t *A, int lda, const int8_t *B, int ldb,
@@ -110,8 +122,15 @@ int gemm_s8s8s32_with_config(int config_id, int b_col_major, int M, int N, int K
  * table order.  Host only; pure after the first call's initialisation. */
 int select_tile_config(int M, int N, int K);
 
-/* Static description of one compiled configuration plus its resource use on
- * the current device (filled in by the initialisation). */
+/* Description of one compiled configuration: the tiling tuple the claims of
+ * patent application CN114238853A select over (claim 2: the thread split
+ * block_m_threads = waves_m * mfma_m and block_n_threads = waves_n * mfma_n;
+ * claims 4 and 5: the per-wave repeats m_tiles and n_tiles, the block tile
+ * block_m x block_n and the K depth block_k; claim 6: the registers each
+ * thread uses, the shared memory (LDS) each block uses and the resulting
+ * resident blocks per compute unit, block_per_cu).  Register and LDS figures
+ * are those of the configuration's column-major-B unpredicated kernel, read
+ * by the build from the compiled code object's metadata. */
 typedef struct {
     int id;
     int family;          /* 0 general tiled kernel, 1 skinny (split-K across waves) kernel */
@@ -122,23 +141,27 @@ typedef struct {
     int stages;          /* LDS stages of the unpredicated column-major-B kernel */
     int threads;
     int lds_bytes;       /* static LDS per block of that kernel */
-    int vgprs;           /* vector registers per lane of the compiled kernel, architectural and
-                            accumulation registers together (the runtime's unified count; 0
-                            before a device is seen) */
-    int agprs;           /* 0: the runtime reports no separate accumulation-register count */
-    int blocks_per_cu;   /* resident blocks per compute unit, from the occupancy query */
+    int vgprs;           /* architectural vector registers per lane of that kernel (rounded up
+                            to a multiple of 4 when accumulation registers follow them) */
+    int agprs;           /* accumulation vector registers per lane of that kernel (the
+                            compiler keeps matrix-core accumulators in either file); the
+                            lane's allocation spans vgprs + agprs registers */
+    int blocks_per_cu;   /* resident blocks per compute unit, from the runtime occupancy query
+                            on the current device (0 before a gfx950 device is seen) */
     int reuse1_id;       /* configuration with the same thread split and m_tiles = n_tiles = 1 */
     int excluded;        /* 1: its reuse scheme (family, m_tiles, n_tiles) was excluded by the
                             performance test of claim 3 (second alternative); the selection drops
                             it at step 2, gemm_s8s8s32_with_config still runs it */
+    int sgprs;           /* scalar registers per wave of that kernel */
 } tdi8_tile_config;
 
 /* Number of compiled configurations; ids are 0 .. count-1. */
 int tile_config_count(void);
 
-/* Copies the description of configuration `id` into *out.  Resource fields
- * are filled only once a gfx950 device has been initialised (they are 0
- * otherwise); no device is needed for the static fields. */
+/* Copies the description of configuration `id` into *out (caller-owned).
+ * Everything but blocks_per_cu is static and needs no device; blocks_per_cu
+ * is filled once a gfx950 device has been initialised (0 otherwise).
+ * Returns TDI8_OK, TDI8_ERR_BAD_CONFIG (unknown id) or TDI8_ERR_NULL_POINTER. */
 int tile_config_info(int id, tdi8_tile_config *out);
 
 /* Hardware description used by the selection. */
@@ -187,6 +210,43 @@ int select_tile_config_for(int M, int N, int K, const tdi8_hw_info *hw,
  * adding into the zeroed C window.  Its K split is
  * a property of the row-major form and is not what this function reports. */
 int tile_config_split_k(int config_id, int M, int N, int K, int num_cu);
+
+/* Kernel forms a gemm call can run (gemm_plan). */
+typedef enum {
+    TDI8_FORM_NONE = 0,             /* M == 0 or N == 0: nothing is enqueued */
+    TDI8_FORM_PREDICATED = 1,       /* register-staged tiled kernel: any K, alignment, leading dims */
+    TDI8_FORM_PIPELINED = 2,        /* LDS-DMA pipelined kernel, whole tiles */
+    TDI8_FORM_PIPELINED_EDGE = 3,   /* the same for sizes that end inside a tile */
+    TDI8_FORM_SPLIT = 4,            /* zero fill, then the K split of the pipelined kernel (whole tiles) */
+    TDI8_FORM_SPLIT_EDGE = 5,       /* zero fill, then the K split of its edge form */
+    TDI8_FORM_SKINNY_DMA = 6,       /* skinny kernel fed by LDS DMA (either B layout) */
+    TDI8_FORM_SKINNY_PREDICATED = 7,/* skinny kernel with masked register loads */
+    TDI8_FORM_SKINNY_ROW_GROUPS = 8 /* zero fill, then the row-major-B column groups of a skinny tile */
+} tdi8_form;
+
+typedef struct {
+    int config_id;   /* configuration that runs (-1 with TDI8_FORM_NONE and no id given) */
+    int form;        /* tdi8_form */
+    int splits;      /* K slices (column groups for TDI8_FORM_SKINNY_ROW_GROUPS); 1 = none */
+    int kernels;     /* kernels enqueued: 2 when a zero fill runs first, else 1 (0 for NONE) */
+    int grid_x, grid_y, threads;  /* launch shape of the product kernel */
+} tdi8_plan;
+
+/* What a gemm call with these arguments would enqueue on the current device,
+ * without enqueueing anything: the configuration (config_id -1: the
+ * selection's, as gemm_s8s8s32 / gemm_s8s8s32_bt; else that id, as
+ * gemm_s8s8s32_with_config), the kernel form and its launch shape.  Patent
+ * application CN114238853A, claim 7: at run time the input size decides the
+ * configuration and its compiled kernel; the launch wrappers of the contest
+ * write-up ("先导杯比赛回顾", NCHW_2_NHWC and 多批次展开的 Im2col 方法)
+ * derive the grid from the sizes before launching.  The form depends on the
+ * sizes and on the alignment of the pointers and leading dimensions, so the
+ * pointers are the ones the call would pass (they are not dereferenced).
+ * Same argument checks and status codes as the gemm call; *out is caller
+ * owned and written only on TDI8_OK.  One decision serves the call and this
+ * query, so the plan is what runs.  Host only; initialises the device. */
+int gemm_plan(int config_id, int b_col_major, int M, int N, int K, const int8_t *A, int lda, const int8_t *B,
+              int ldb, const int32_t *C, int ldc, tdi8_plan *out);
 
 /* ---- int8 2-D convolution (implicit GEMM on the same kernels) ----------------
  *
@@ -251,10 +311,16 @@ int conv2d_validate(int N, int H, int W, int C, int K, int R, int S,
 int tdi8_validate(int b_col_major, int M, int N, int K, const int8_t *A, int lda,
                   const int8_t *B, int ldb, const int32_t *C, int ldc);
 
-/* Static string for a status code. */
+/* Static string for a status code (never NULL; "unknown status" for a value
+ * outside tdi8_status; the caller must not free it).  The contest write-up's
+ * launch wrappers ("先导杯比赛回顾", NCHW_2_NHWC and 多批次展开的 Im2col 方法)
+ * read hipGetLastError after each launch and print its error string; a
+ * library prints nothing, so the status code and this text take its place. */
 const char *tdi8_status_string(int status);
 
-/* hipError_t of the last failed HIP call made by this thread (0 if none). */
+/* hipError_t of the last failed HIP call made by this thread (0 if none):
+ * the error those launch wrappers obtain from hipGetLastError, kept per
+ * thread for the caller after an entry point returned TDI8_ERR_HIP. */
 int tdi8_last_hip_error(void);
 
 #ifdef __cplusplus

@@ -53,11 +53,28 @@ Readings:
       the maximum, compared exactly by cross-multiplication.
   claim 6: Launch_kernel_times = ceil(Thread_Blocks / (num_cu * blocks_per_cu)),
       the number of rounds of resident blocks.  Step 5 keeps the minimum.
+      block_per_cu (block_per_cu() below) is the smaller of the claim's two
+      quotients: the register quotient, registers a thread may hold over the
+      registers it uses, and the shared-memory quotient, the shared memory of
+      a compute unit over what one block uses.  On CDNA4 a lane may hold 512
+      vector registers (both register files together), allocated in granules
+      of 8, so the register quotient counts waves per SIMD (at most the
+      SIMD's 8 wave slots); a compute unit has 4 SIMDs, so it holds
+      floor(4 * waves per SIMD / waves per block) blocks by registers, and
+      floor(160 KiB / LDS per block) by LDS.
   Remaining ties: first in table order.
-  step 1 on CDNA4 (an addition, not in the claims): a configuration whose
-      block tile overhangs the problem (BM above max(m, the family's smallest
-      BM), or BN likewise) only adds zero rows or columns and is left out, at
-      step 1 and among the fallback's reuse-1 siblings, unless none is left.
+
+Rules of the CDNA4 re-derivation that are not steps of the claims (the pages
+print no selector output, so against the pages these are PARITY UNPINNED; the
+tests pin them only by worked examples of the rules themselves):
+  * no_overhang: the step-1 filter on block tiles larger than the problem;
+  * the skinny route after claim 4's fallback (m or n <= skinny_max_m);
+  * split_k: the K split after the five steps (the contest write-up's Split K
+    paragraph gives the atomics, not the slice count), including its measured
+    minimum of eight K tiles per slice.
+The steps of the claims and claim 6's block_per_cu are pinned: the worked
+examples of the claims' steps, and block_per_cu against the device's runtime
+occupancy query for every compiled configuration (a GPU test).
 """
 from __future__ import annotations
 
@@ -74,6 +91,31 @@ class Hw:
     max_threads_per_block: int = 1024
     min_active_threads: int = 256
     skinny_max_m: int = 32
+
+
+@dataclass(frozen=True)
+class CuLimits:
+    """Per-compute-unit limits that claim 6's quotients divide (CDNA4 values)."""
+    simds: int = 4                 # SIMDs per compute unit
+    regs_per_lane: int = 512       # vector registers a lane may hold, both files together
+    reg_granule: int = 8           # allocation granule of vector registers
+    wave_slots: int = 8            # waves one SIMD holds at once
+    lds_bytes: int = 160 * 1024    # LDS (shared memory) of one compute unit
+    wave_size: int = 64
+
+
+def block_per_cu(vgprs: int, agprs: int, lds_per_block: int, threads: int, lim: CuLimits = CuLimits()) -> int:
+    """Claim 6: blocks resident on one compute unit, the minimum of the
+    register quotient and the shared-memory quotient.  vgprs + agprs are the
+    vector registers a lane of the kernel uses (architectural, rounded to a
+    multiple of 4 when accumulation registers follow, then accumulation)."""
+    used = vgprs + agprs
+    alloc = ceil_div(used, lim.reg_granule) * lim.reg_granule
+    waves_per_simd = lim.wave_slots if alloc == 0 else min(lim.wave_slots, lim.regs_per_lane // alloc)
+    waves_per_block = ceil_div(threads, lim.wave_size)
+    by_regs = lim.simds * waves_per_simd // waves_per_block
+    by_lds = lim.lds_bytes // lds_per_block if lds_per_block > 0 else by_regs
+    return min(by_regs, by_lds)
 
 
 @dataclass(frozen=True)
@@ -163,7 +205,8 @@ def _steps_4_5(cands: list[Cfg], m: int, n: int, hw: Hw, trace: dict) -> Cfg:
 
 def split_k(c: Cfg, m: int, n: int, k: int, num_cu: int) -> int:
     """K slices for configuration c when its unpredicated form runs (K a
-    multiple of 16 bytes): a CDNA4 addition after the five steps, from the
+    multiple of 16 bytes).  CDNA4 RULE, NOT A STEP OF THE CLAIMS (parity
+    unpinned against the pages): an addition after the five steps, from the
     contest write-up's "Split K" paragraph (partial sums over K slices added
     with integer atomics).  Reading: the slice count s is a power of two, the
     largest with tiles * s <= num_cu (tiles counting the partial ones at the
@@ -182,7 +225,8 @@ def split_k(c: Cfg, m: int, n: int, k: int, num_cu: int) -> int:
 
 
 def no_overhang(cands: list[Cfg], m: int, n: int, table: list[Cfg]) -> list[Cfg]:
-    """CDNA4 addition to step 1: keep the configurations whose block tile is
+    """CDNA4 RULE, NOT A STEP OF THE CLAIMS (parity unpinned against the
+    pages), added to step 1: keep the configurations whose block tile is
     no taller than max(m, smallest block height of the general family) and
     no wider than max(n, smallest width); all of them if none is."""
     gen = [c for c in table if c.family == "general"]
@@ -213,7 +257,9 @@ def select(m: int, n: int, k: int, hw: Hw, table: list[Cfg]) -> Result:
                 s3.append(d)
         s3 = no_overhang(sorted(s3, key=lambda c: c.id), m, n, table)
         if m <= hw.skinny_max_m or n <= hw.skinny_max_m:
-            # a small m picks by block height, else a small n by block width
+            # CDNA4 RULE, NOT A STEP OF THE CLAIMS (parity unpinned against the
+            # pages): the skinny route.  A small m picks by block height, else
+            # a small n by block width
             ext = (lambda c: c.BM) if m <= hw.skinny_max_m else (lambda c: c.BN)
             small = m if m <= hw.skinny_max_m else n
             skinny = [c for c in table if c.family == "skinny" and ext(c) >= small and step2_ok(c, hw)]

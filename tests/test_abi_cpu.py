@@ -8,7 +8,7 @@ import re
 import pytest
 
 import tiled_dense_int8_amd as t
-from oracle.selector import Cfg, Hw, select
+from oracle.selector import Cfg, CuLimits, Hw, block_per_cu, select
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tdi8.h")
 
@@ -115,23 +115,97 @@ def oracle_table(bpc):
                 c.block_k, c.threads, bpc[c.id], c.stages, bool(c.excluded)) for c in library_table()]
 
 
-def fake_bpc(lds_per_cu=160 * 1024, waves_per_cu=32):
-    """Resident blocks per CU from LDS and wave slots, a stand-in for the occupancy query."""
-    out = []
-    for c in library_table():
-        by_lds = lds_per_cu // c.lds_bytes
-        by_waves = waves_per_cu // (c.threads // 64)
-        out.append(max(0, min(by_lds, by_waves, 8)))
-    return out
+def claim6_bpc(lim=CuLimits()):
+    """Resident blocks per CU of every compiled configuration by claim 6's
+    quotients (the oracle's block_per_cu) from the registers and LDS the
+    build read out of each kernel, on described compute-unit limits."""
+    return [block_per_cu(c.vgprs, c.agprs, c.lds_bytes, c.threads, lim) for c in library_table()]
 
 
 HARDWARE = [
-    (Hw(256, 1024, 256, 32), fake_bpc()),
+    (Hw(256, 1024, 256, 32), claim6_bpc()),
     (Hw(256, 1024, 256, 32), [1] * 64),
-    (Hw(304, 1024, 256, 32), fake_bpc(64 * 1024)),
-    (Hw(80, 256, 128, 16), fake_bpc(64 * 1024, 16)),
-    (Hw(256, 1024, 1024, 32), fake_bpc()),
+    (Hw(304, 1024, 256, 32), claim6_bpc(CuLimits(lds_bytes=64 * 1024))),
+    (Hw(80, 256, 128, 16), claim6_bpc(CuLimits(lds_bytes=64 * 1024, regs_per_lane=256, wave_slots=4))),
+    (Hw(256, 1024, 1024, 32), claim6_bpc()),
 ]
+
+
+def test_kernel_resources_from_the_build():
+    """Register and LDS figures come from the compiled code objects: the
+    general kernels' LDS is exactly their stage buffers, every kernel fits
+    the 512 registers of a lane, and architectural registers that precede
+    accumulation registers are a multiple of 4."""
+    for c in library_table():
+        assert c.vgprs > 0 and c.sgprs > 0 and c.agprs >= 0
+        assert c.vgprs + c.agprs <= 512
+        if c.agprs:
+            assert c.vgprs % 4 == 0
+        assert 0 < c.lds_bytes <= 160 * 1024
+    # the 4-wave 256 x 256 tiles hold 16 accumulator tiles of 16 registers per lane
+    tab = library_table()
+    assert any(c.agprs == 256 for c in tab if c.block_m == c.block_n == 256 and c.threads == 256)
+
+
+def test_claim6_block_per_cu_worked_examples():
+    """Claim 6's quotients worked by hand on CDNA4's limits (512 registers a
+    lane in granules of 8, 8 wave slots per SIMD, 4 SIMDs, 160 KiB LDS)."""
+    # 216 registers -> 2 waves per SIMD -> 8 waves per CU -> one 8-wave block; LDS 160/128 -> 1
+    assert block_per_cu(216, 0, 131072, 512) == 1
+    # 56 + 16 = 72 registers -> 7 waves per SIMD -> 28 waves -> 7 four-wave blocks; LDS 160/32 -> 5
+    assert block_per_cu(56, 16, 32768, 256) == 5
+    # the same without LDS: the register quotient decides
+    assert block_per_cu(56, 16, 0, 256) == 7
+    # 83 registers allocate 88 -> 5 waves per SIMD -> 20 waves -> two 8-wave blocks
+    assert block_per_cu(83, 0, 1024, 512) == 2
+    # few registers: the 8 wave slots cap the quotient (32 waves -> two 16-wave blocks)
+    assert block_per_cu(38, 0, 1024, 1024) == 2
+    # 104 + 256 = 360 registers -> one wave per SIMD -> one 4-wave block
+    assert block_per_cu(104, 256, 65536, 256) == 1
+    # a kernel too large for the hardware described gets 0
+    assert block_per_cu(300, 0, 1024, 512, CuLimits(regs_per_lane=256)) == 0
+    assert block_per_cu(64, 0, 200 * 1024, 256) == 0
+    # granule: 129 registers allocate 136 -> 3 waves, 128 allocate 128 -> 4
+    assert block_per_cu(129, 0, 0, 256) == 3 and block_per_cu(128, 0, 0, 256) == 4
+
+
+def test_gemm_plan_host_checks():
+    """gemm_plan refuses bad arguments with the gemm call's status codes,
+    before any device work, and an empty product plans nothing."""
+    with pytest.raises(t.TDI8Error) as e:
+        t.gemm_plan(-1, 1, -1, 4, 4, A, 4, B, 4, C, 4)
+    assert e.value.status == t.ERR_INVALID_VALUE
+    with pytest.raises(t.TDI8Error) as e:
+        t.gemm_plan(99, 1, 4, 4, 4, A, 4, B, 4, C, 4)
+    assert e.value.status == t.ERR_BAD_CONFIG
+    with pytest.raises(t.TDI8Error) as e:
+        t.gemm_plan(-1, 0, 4, 4, 4, A, 4, B, 4, A + 2, 4)
+    assert e.value.status == t.ERR_ALIASING
+    p = t.gemm_plan(-1, 1, 0, 4, 4, 0, 4, 0, 4, 0, 4)
+    assert (p.form, p.kernels, p.config_id) == (t.FORM_NONE, 0, -1)
+    assert t._lib.gemm_plan(-1, 1, 4, 4, 4, A, 4, B, 4, C, 4, None) == t.ERR_NULL_POINTER
+
+
+def test_int_arguments_beyond_int32_are_refused():
+    """ctypes would wrap a Python int past 2**31 - 1 silently (2**32 + 5
+    arrives as 5); the binding refuses it before calling the library."""
+    for bad in (2 ** 31, 2 ** 32 + 5, -2 ** 31 - 1):
+        with pytest.raises(ValueError):
+            t.gemm_s8s8s32(bad, 4, 4, A, 4, B, 4, C, 4, 0)
+        with pytest.raises(ValueError):
+            t.gemm_s8s8s32_bt(4, 4, 4, A, bad, B, 4, C, 4, 0)
+        with pytest.raises(ValueError):
+            t.gemm_s8s8s32_with_config(0, 1, 4, 4, 4, A, 4, B, 4, C, bad, 0)
+        with pytest.raises(ValueError):
+            t.select_tile_config(4, bad, 4)
+        with pytest.raises(ValueError):
+            t.tdi8_validate(1, 4, 4, bad, A, 4, B, 4, C, 4)
+        with pytest.raises(ValueError):
+            t.conv2d_s8s8s32_nhwc(1, bad, 8, 16, 4, 3, 3, 1, 1, 1, 1, 1, 1, A, B, C, 0)
+        with pytest.raises(ValueError):
+            t.conv2d_output_extent(bad, 3, 1, 1, 1)
+    # the largest int passes through to the library's own checks
+    assert t.gemm_s8s8s32(t.INT_MAX, 4, 4, A, 3, B, 4, C, 4, 0) == t.ERR_INVALID_VALUE  # lda < K
 SHAPES = [(m, n) for m in (1, 7, 16, 17, 32, 33, 64, 100, 256, 1000, 4096, 16384)
           for n in (1, 16, 100, 256, 3000, 4096, 8192, 16384)]
 
@@ -155,10 +229,10 @@ def test_selection_matches_oracle_reading(hw_index):
 
 
 def test_mi355x_expectations():
-    """With the MI355X description and LDS/wave-slot occupancy, the selection
+    """With the MI355X description and claim 6's occupancy, the selection
     routes the five workloads as the method intends."""
     hwc = t.HwInfo(256, 1024, 256, 32)
-    bpc = fake_bpc()
+    bpc = claim6_bpc()
     tab = library_table()
     s = t.select_tile_config_for(4096, 4096, 4096, hwc, bpc)
     assert s.route == t.ROUTE_GENERAL and (tab[s.id].block_m, tab[s.id].block_n) == (256, 256)

@@ -111,11 +111,15 @@ def test_random_k_split_shapes(lib, bcm):
         config = None if rng.random() < 0.5 else int(rng.choice(general))
         cid = t.select_tile_config(M, N, K) if config is None else config
         s = t.tile_config_split_k(cid, M, N, K, cus)
-        split_cases += s > 1
         lda = K + int(16 * rng.integers(0, 3))
         ldb = (K if bcm else N) + int(16 * rng.integers(0, 3))
         ldc = N + int(4 * rng.integers(0, 3)) + (4 - N % 4) % 4
         A, B = synthetic.gemm_inputs(M, N, K, seed=3000 + i)
         case = DeviceCase(A, B, bcm, lda=lda, ldb=ldb, ldc=ldc)
+        # count a case as split only if the call really runs a split kernel
+        p = t.gemm_plan(-1 if config is None else config, bcm, M, N, K, case.A_ptr, lda, case.B_ptr, ldb,
+                        case.C_ptr, ldc)
+        assert p.config_id == cid and p.splits == s, (i, p.as_dict(), s)
+        split_cases += p.form in (t.FORM_SPLIT, t.FORM_SPLIT_EDGE)
         check_case(case, f"random split[{i}] {M}x{N}x{K} cfg{cid} x{s}", config=config)
     assert split_cases >= 20, split_cases

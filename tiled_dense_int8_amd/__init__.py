@@ -38,7 +38,7 @@ class TileConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "id", "family", "mfma_m", "mfma_n", "mfma_k", "waves_m", "waves_n", "waves_k",
         "m_tiles", "n_tiles", "block_m", "block_n", "block_k", "stages", "threads", "lds_bytes",
-        "vgprs", "agprs", "blocks_per_cu", "reuse1_id", "excluded")]
+        "vgprs", "agprs", "blocks_per_cu", "reuse1_id", "excluded", "sgprs")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -53,6 +53,18 @@ class Selection(ctypes.Structure):
     _fields_ = [("id", ctypes.c_int), ("route", ctypes.c_int), ("survivors", ctypes.c_int * 5)]
 
 
+FORM_NONE, FORM_PREDICATED, FORM_PIPELINED, FORM_PIPELINED_EDGE, FORM_SPLIT, FORM_SPLIT_EDGE, \
+    FORM_SKINNY_DMA, FORM_SKINNY_PREDICATED, FORM_SKINNY_ROW_GROUPS = range(9)
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "config_id", "form", "splits", "kernels", "grid_x", "grid_y", "threads")]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
 _i, _p = ctypes.c_int, ctypes.c_void_p
 _GEMM_ARGS = [_i, _i, _i, _p, _i, _p, _i, _p, _i, _p]
 _SIGNATURES = {
@@ -63,6 +75,7 @@ _SIGNATURES = {
     "tile_config_count": (_i, []),
     "tile_config_info": (_i, [_i, ctypes.POINTER(TileConfig)]),
     "tile_config_split_k": (_i, [_i, _i, _i, _i, _i]),
+    "gemm_plan": (_i, [_i, _i, _i, _i, _i, _p, _i, _p, _i, _p, _i, ctypes.POINTER(Plan)]),
     "select_tile_config_for": (_i, [_i, _i, _i, ctypes.POINTER(HwInfo), ctypes.POINTER(_i),
                                     ctypes.POINTER(Selection)]),
     "tdi8_validate": (_i, [_i, _i, _i, _i, _p, _i, _p, _i, _p, _i]),
@@ -91,26 +104,54 @@ class TDI8Error(RuntimeError):
         super().__init__(f"tdi8 status {status}: {msg}")
 
 
+INT_MAX = 2 ** 31 - 1
+
+
+def _int32(**vals) -> None:
+    """The C entry points take int arguments; ctypes would wrap a larger
+    Python int silently (2**32 + 5 arrives as 5), so refuse it here."""
+    for name, v in vals.items():
+        if not -2 ** 31 <= int(v) <= INT_MAX:
+            raise ValueError(f"{name} = {v} does not fit the library's int arguments (|value| < 2**31)")
+
+
 # ----- the C entry points, same names and arguments -------------------------------
 
 def gemm_s8s8s32(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    _int32(M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     return _lib.gemm_s8s8s32(M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
 def gemm_s8s8s32_bt(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    _int32(M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     return _lib.gemm_s8s8s32_bt(M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
 def gemm_s8s8s32_with_config(config_id, b_col_major, M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    _int32(config_id=config_id, M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     return _lib.gemm_s8s8s32_with_config(config_id, 1 if b_col_major else 0, M, N, K, A, lda, B, ldb,
                                          C, ldc, stream)
 
 
+def gemm_plan(config_id, b_col_major, M, N, K, A, lda, B, ldb, C, ldc) -> Plan:
+    """What the gemm call with these arguments would enqueue (config_id -1:
+    the selected configuration); raises TDI8Error on a bad argument."""
+    _int32(config_id=config_id, M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
+    out = Plan()
+    st = _lib.gemm_plan(config_id, 1 if b_col_major else 0, M, N, K, A, lda, B, ldb, C, ldc,
+                        ctypes.byref(out))
+    if st != OK:
+        raise TDI8Error(st)
+    return out
+
+
 def select_tile_config(M, N, K) -> int:
+    _int32(M=M, N=N, K=K)
     return _lib.select_tile_config(M, N, K)
 
 
 def tile_config_split_k(config_id, M, N, K, num_cu) -> int:
+    _int32(config_id=config_id, M=M, N=N, K=K, num_cu=num_cu)
     return _lib.tile_config_split_k(config_id, M, N, K, num_cu)
 
 
@@ -127,6 +168,7 @@ def tile_config_info(config_id: int) -> TileConfig:
 
 
 def select_tile_config_for(M, N, K, hw: HwInfo, blocks_per_cu) -> Selection:
+    _int32(M=M, N=N, K=K)
     arr = (ctypes.c_int * tile_config_count())(*blocks_per_cu)
     out = Selection()
     st = _lib.select_tile_config_for(M, N, K, ctypes.byref(hw), arr, ctypes.byref(out))
@@ -136,6 +178,7 @@ def select_tile_config_for(M, N, K, hw: HwInfo, blocks_per_cu) -> Selection:
 
 
 def tdi8_validate(b_col_major, M, N, K, A, lda, B, ldb, C, ldc) -> int:
+    _int32(M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     return _lib.tdi8_validate(1 if b_col_major else 0, M, N, K, A, lda, B, ldb, C, ldc)
 
 
@@ -190,6 +233,7 @@ def gemm(A: "torch.Tensor", B: "torch.Tensor", b_col_major: bool, out: "torch.Te
     if out.dtype != torch.int32 or out.dim() != 2 or tuple(out.shape) != (M, N) or out.stride(1) != 1:
         raise ValueError("out must be int32 (M, N) with unit column stride")
     lda, ldb, ldc = max(A.stride(0), 1), max(B.stride(0), 1), max(out.stride(0), 1)
+    _int32(M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     with torch.cuda.device(dev):
         s = _stream_handle(stream)
         if config is None:
@@ -205,27 +249,38 @@ def gemm(A: "torch.Tensor", B: "torch.Tensor", b_col_major: bool, out: "torch.Te
 
 # ---- convolution ---------------------------------------------------------------
 
+def _conv_int32(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w) -> None:
+    _int32(N=N, H=H, W=W, C=C, K=K, R=R, S=S, pad_h=pad_h, pad_w=pad_w, stride_h=stride_h,
+           stride_w=stride_w, dil_h=dil_h, dil_w=dil_w)
+
+
 def conv2d_s8s8s32_nhwc(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w,
                         x, w, y, stream=0) -> int:
+    _conv_int32(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w)
     return _lib.conv2d_s8s8s32_nhwc(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w,
                                     x, w, y, stream)
 
 
 def conv2d_s8s8s32_nhwc_with_config(config_id, N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w,
                                     dil_h, dil_w, x, w, y, stream=0) -> int:
+    _int32(config_id=config_id)
+    _conv_int32(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w)
     return _lib.conv2d_s8s8s32_nhwc_with_config(config_id, N, H, W, C, K, R, S, pad_h, pad_w, stride_h,
                                                 stride_w, dil_h, dil_w, x, w, y, stream)
 
 
 def conv2d_select_config(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w) -> int:
+    _conv_int32(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w)
     return _lib.conv2d_select_config(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w)
 
 
 def conv2d_output_extent(H, R, pad, stride, dil) -> int:
+    _int32(H=H, R=R, pad=pad, stride=stride, dil=dil)
     return _lib.conv2d_output_extent(H, R, pad, stride, dil)
 
 
 def conv2d_validate(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, x, w, y) -> int:
+    _conv_int32(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w)
     return _lib.conv2d_validate(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, x, w, y)
 
 

@@ -63,8 +63,6 @@ struct DeviceState {
     int hip_error = 0;
     tdi8_hw_info hw{};
     int bpc[TDI8_NUM_CONFIGS] = {};
-    int regs[TDI8_NUM_CONFIGS] = {};
-    int lds[TDI8_NUM_CONFIGS] = {};
 };
 
 DeviceState g_devices[kMaxDevices];
@@ -88,13 +86,6 @@ void init_device(DeviceState &ds, int dev) {
     for (int id = 0; id < TDI8_NUM_CONFIGS; ++id) {
         const StaticCfg c = static_cfg(id);
         const void *k = kernels()[id].kernel[1][1];
-        hipFuncAttributes fa;
-        e = hipFuncGetAttributes(&fa, k);
-        if (e != hipSuccess) {
-            ds.status = TDI8_ERR_HIP;
-            ds.hip_error = static_cast<int>(e);
-            return;
-        }
         int nb = 0;
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, c.threads, 0);
         if (e != hipSuccess) {
@@ -103,8 +94,6 @@ void init_device(DeviceState &ds, int dev) {
             return;
         }
         ds.bpc[id] = nb;
-        ds.regs[id] = fa.numRegs;
-        ds.lds[id] = static_cast<int>(fa.sharedSizeBytes);
     }
 }
 
@@ -132,24 +121,20 @@ DeviceState *current_device(int *status) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Zero the C window, then launch a K-split kernel whose blocks (one per tile
-// and K slice) add their partial sums into it.
-int launch_split(const void *kernel, GemmArgs &g, dim3 grid, dim3 block, hipStream_t stream) {
-    const int64_t quads = static_cast<int64_t>(g.M) * ((g.N + 3) / 4);
-    const unsigned zb = static_cast<unsigned>(quads / 256 + 1 < 2048 ? quads / 256 + 1 : 2048);
-    void *args[] = {&g};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&zero_c_kernel), dim3(zb), dim3(256), args, 0,
-                                   stream);
-    if (e != hipSuccess) return hip_fail(e);
-    e = hipLaunchKernel(kernel, grid, block, args, 0, stream);
-    if (e != hipSuccess) return hip_fail(e);
-    return TDI8_OK;
-}
+// Which kernel runs a call, on which grid: one decision, shared by the launch
+// and the gemm_plan query, so that what the query reports is what runs.
+struct Plan {
+    int form = TDI8_FORM_NONE;
+    const void *kernel = nullptr;
+    bool zero_first = false;  // a fill kernel zeroes the C window first (K split)
+    dim3 grid, block;
+    GemmArgs g{};
+};
 
-int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
-           int32_t *C, int ldc, hipStream_t stream, int num_cu) {
+int make_plan(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
+              int32_t *C, int ldc, int num_cu, Plan *p) {
     const StaticCfg c = static_cfg(id);
-    GemmArgs g;
+    GemmArgs &g = p->g;
     g.splits = 1;
     g.A = A;
     g.B = B;
@@ -160,69 +145,92 @@ int launch(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, cons
     g.M = M;
     g.N = N;
     g.K = K;
+    const int b = bcol ? 1 : 0;
     const bool c_ok = aligned(C, 16) && ldc % 4 == 0;
     const bool a_ok = aligned(A, 16) && lda % 16 == 0;
-    dim3 grid, block(c.threads);
-    bool fast, edge = false;
+    const bool b_ok = aligned(B, 16) && ldb % 16 == 0;
+    p->block = dim3(c.threads);
     if (c.family == 0) {
         const int64_t tm = (M + static_cast<int64_t>(c.bm) - 1) / c.bm;
         const int64_t tn = (N + static_cast<int64_t>(c.bn) - 1) / c.bn;
         if (tm * tn > INT_MAX / c.threads) return TDI8_ERR_INVALID_VALUE;
         g.tiles_m = static_cast<int>(tm);
         g.tiles_n = static_cast<int>(tn);
-        grid = dim3(static_cast<unsigned>(tm * tn));
         // both B layouts are moved by 16-byte LDS DMA loads in the fast form;
         // chunks outside the operands read a zero chunk and stores are
         // masked, so M and N are free and K (and, row-major B, N) need only
         // be multiples of 16 (the edge form: sizes that end inside a tile);
         // the K split runs in the whole-tile form when M, N and every slice
         // are whole tiles, else in the edge form (slices of 16-byte chunks)
-        const bool b_ok = aligned(B, 16) && ldb % 16 == 0;
-        fast = K % 16 == 0 && (bcol || N % 16 == 0) && a_ok && b_ok && c_ok;
-        edge = fast && (M % c.bm != 0 || N % c.bn != 0 || K % c.bk != 0);
+        const bool fast = K % 16 == 0 && (bcol || N % 16 == 0) && a_ok && b_ok && c_ok;
+        const bool edge = fast && (M % c.bm != 0 || N % c.bn != 0 || K % c.bk != 0);
         if (fast) g.splits = split_k_for(c, M, N, K, num_cu);
         if (g.splits > 1) {
             const bool whole = !edge && K % (g.splits * c.bk) == 0;
-            const void *k = whole ? kernels()[id].split[bcol ? 1 : 0] : kernels()[id].split_edge[bcol ? 1 : 0];
-            return launch_split(k, g, dim3(static_cast<unsigned>(tm * tn * g.splits)), block, stream);
+            p->form = whole ? TDI8_FORM_SPLIT : TDI8_FORM_SPLIT_EDGE;
+            p->kernel = whole ? kernels()[id].split[b] : kernels()[id].split_edge[b];
+            p->zero_first = true;
+            p->grid = dim3(static_cast<unsigned>(tm * tn * g.splits));
+        } else {
+            p->form = !fast ? TDI8_FORM_PREDICATED : edge ? TDI8_FORM_PIPELINED_EDGE : TDI8_FORM_PIPELINED;
+            p->kernel = edge ? kernels()[id].edge[b] : kernels()[id].kernel[b][fast ? 1 : 0];
+            p->grid = dim3(static_cast<unsigned>(tm * tn));
         }
-    } else {
-        // the unpredicated forms move B by 16-byte LDS DMA loads in both
-        // layouts; a ragged M (M < 16 included) reads zero chunks past M, and
-        // a last, partial K chunk zero pieces past K (K a multiple of 16)
-        const bool dma_ok = a_ok && aligned(B, 16) && ldb % 16 == 0 && c_ok;
-        fast = N % c.bn == 0 && K % 16 == 0 && dma_ok;
-        // Row-major B: the column-group form (kernel_table.h) when N and K
-        // are whole 16-byte chunks (the edge form: a last group may end
-        // inside its 128 columns, a K slice inside a K tile; the last slices
-        // may be shorter) and N is whole groups or more than two of them (a
-        // narrow N would leave most of every group's columns empty:
-        // 4096 x 16 x 4096 took 29 us that way against 6 in the per-tile form).
-        const int groups = kRrGroupCols / c.bn;
-        if (!bcol && dma_ok && (N % kRrGroupCols == 0 || N > 2 * kRrGroupCols) && N % 16 == 0 && K % 16 == 0) {
-            const int64_t tm = (M + static_cast<int64_t>(c.bm) - 1) / c.bm;
-            const int64_t tn = (N + kRrGroupCols - 1) / kRrGroupCols;
-            if (tm * tn * groups <= INT_MAX / 512) {
-                g.tiles_m = static_cast<int>(tm);
-                g.tiles_n = static_cast<int>(tn);
-                g.splits = groups;
-                return launch_split(kernels()[id].rr_group, g, dim3(static_cast<unsigned>(tm * tn * groups)),
-                                    dim3(512), stream);
-            }
-        }
-        // the predicated row-major form covers 64 columns per block
-        const int bn = (bcol || fast) ? c.bn : 64;
-        const int64_t tm = (M + static_cast<int64_t>(c.bm) - 1) / c.bm;
-        const int64_t tn = (N + static_cast<int64_t>(bn) - 1) / bn;
-        if (tm > 65535) return TDI8_ERR_BAD_CONFIG;
-        if (tn > INT_MAX / c.threads) return TDI8_ERR_INVALID_VALUE;
-        g.tiles_m = static_cast<int>(tm);
-        g.tiles_n = static_cast<int>(tn);
-        grid = dim3(static_cast<unsigned>(tn), static_cast<unsigned>(tm));
+        return TDI8_OK;
     }
-    const void *k = edge ? kernels()[id].edge[bcol ? 1 : 0] : kernels()[id].kernel[bcol ? 1 : 0][fast ? 1 : 0];
-    void *args[] = {&g};
-    hipError_t e = hipLaunchKernel(k, grid, block, args, 0, stream);
+    // Skinny family.  The unpredicated forms move B by 16-byte LDS DMA loads
+    // in both layouts; a ragged M (M < 16 included) reads zero chunks past M,
+    // and a last, partial K chunk zero pieces past K (K a multiple of 16).
+    const bool dma_ok = a_ok && b_ok && c_ok;
+    const bool fast = N % c.bn == 0 && K % 16 == 0 && dma_ok;
+    // Row-major B: the column-group form (kernel_table.h) when N and K are
+    // whole 16-byte chunks (the edge form: a last group may end inside its
+    // 128 columns, a K slice inside a K tile; the last slices may be
+    // shorter) and N is whole groups or more than two of them (a narrow N
+    // would leave most of every group's columns empty: 4096 x 16 x 4096 took
+    // 29 us that way against 6 in the per-tile form).
+    const int groups = kRrGroupCols / c.bn;
+    if (!bcol && dma_ok && (N % kRrGroupCols == 0 || N > 2 * kRrGroupCols) && N % 16 == 0 && K % 16 == 0) {
+        const int64_t tm = (M + static_cast<int64_t>(c.bm) - 1) / c.bm;
+        const int64_t tn = (N + kRrGroupCols - 1) / kRrGroupCols;
+        if (tm * tn * groups <= INT_MAX / 512) {
+            g.tiles_m = static_cast<int>(tm);
+            g.tiles_n = static_cast<int>(tn);
+            g.splits = groups;
+            p->form = TDI8_FORM_SKINNY_ROW_GROUPS;
+            p->kernel = kernels()[id].rr_group;
+            p->zero_first = true;
+            p->grid = dim3(static_cast<unsigned>(tm * tn * groups));
+            p->block = dim3(512);
+            return TDI8_OK;
+        }
+    }
+    // the predicated row-major form covers 64 columns per block
+    const int bn = (bcol || fast) ? c.bn : 64;
+    const int64_t tm = (M + static_cast<int64_t>(c.bm) - 1) / c.bm;
+    const int64_t tn = (N + static_cast<int64_t>(bn) - 1) / bn;
+    if (tm > 65535) return TDI8_ERR_BAD_CONFIG;
+    if (tn > INT_MAX / c.threads) return TDI8_ERR_INVALID_VALUE;
+    g.tiles_m = static_cast<int>(tm);
+    g.tiles_n = static_cast<int>(tn);
+    p->form = fast ? TDI8_FORM_SKINNY_DMA : TDI8_FORM_SKINNY_PREDICATED;
+    p->kernel = kernels()[id].kernel[b][fast ? 1 : 0];
+    p->grid = dim3(static_cast<unsigned>(tn), static_cast<unsigned>(tm));
+    return TDI8_OK;
+}
+
+// Enqueue a plan: for a K split, first the fill kernel that zeroes the C
+// window, whose blocks then add their partial sums into it.
+int run_plan(Plan &p, hipStream_t stream) {
+    void *args[] = {&p.g};
+    hipError_t e;
+    if (p.zero_first) {
+        const int64_t quads = static_cast<int64_t>(p.g.M) * ((p.g.N + 3) / 4);
+        const unsigned zb = static_cast<unsigned>(quads / 256 + 1 < 2048 ? quads / 256 + 1 : 2048);
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&zero_c_kernel), dim3(zb), dim3(256), args, 0, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    e = hipLaunchKernel(p.kernel, p.grid, p.block, args, 0, stream);
     if (e != hipSuccess) return hip_fail(e);
     return TDI8_OK;
 }
@@ -242,7 +250,10 @@ int gemm_entry(int cfg, int bcol, int M, int N, int K, const int8_t *A, int lda,
         id = select_config(M, N, K, ds->hw, ds->bpc, nullptr);
         if (id < 0) return id;
     }
-    return launch(id, bcol, M, N, K, A, lda, B, ldb, C, ldc, stream, ds->hw.num_cu);
+    Plan p;
+    st = make_plan(id, bcol, M, N, K, A, lda, B, ldb, C, ldc, ds->hw.num_cu, &p);
+    if (st != TDI8_OK) return st;
+    return run_plan(p, stream);
 }
 
 int64_t conv_extent(int64_t H, int64_t R, int64_t pad, int64_t stride, int64_t dil) {
@@ -455,6 +466,7 @@ int tile_config_info(int id, tdi8_tile_config *out) {
     if (id < 0 || id >= TDI8_NUM_CONFIGS) return TDI8_ERR_BAD_CONFIG;
     if (!out) return TDI8_ERR_NULL_POINTER;
     const StaticCfg c = static_cfg(id);
+    const KernelResources &r = kKernelResources[id];
     tdi8_tile_config t{};
     t.id = id;
     t.family = c.family;
@@ -471,21 +483,54 @@ int tile_config_info(int id, tdi8_tile_config *out) {
     t.block_k = c.bk;
     t.stages = c.stages;
     t.threads = c.threads;
-    t.lds_bytes = c.lds_bytes;
+    t.lds_bytes = r.lds_bytes;
+    t.vgprs = r.unified_vgprs - r.agprs;
+    t.agprs = r.agprs;
+    t.sgprs = r.sgprs;
     t.reuse1_id = c.reuse1_id;
     t.excluded = c.excluded;
     int dev = -1;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
         int st = TDI8_OK;
         DeviceState *ds = current_device(&st);
-        if (ds) {
-            t.vgprs = ds->regs[id];
-            t.agprs = 0;
-            t.blocks_per_cu = ds->bpc[id];
-            if (ds->lds[id] > 0) t.lds_bytes = ds->lds[id];
-        }
+        if (ds) t.blocks_per_cu = ds->bpc[id];
     }
     *out = t;
+    return TDI8_OK;
+}
+
+int gemm_plan(int config_id, int b_col_major, int M, int N, int K, const int8_t *A, int lda, const int8_t *B,
+              int ldb, const int32_t *C, int ldc, tdi8_plan *out) {
+    if (!out) return TDI8_ERR_NULL_POINTER;
+    if (config_id < -1 || config_id >= TDI8_NUM_CONFIGS) return TDI8_ERR_BAD_CONFIG;
+    const int bcol = b_col_major ? 1 : 0;
+    int st = tdi8_validate(bcol, M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != TDI8_OK) return st;
+    tdi8_plan r{};
+    r.config_id = config_id;
+    r.form = TDI8_FORM_NONE;
+    if (M == 0 || N == 0) {
+        *out = r;
+        return TDI8_OK;
+    }
+    DeviceState *ds = current_device(&st);
+    if (!ds) return st;
+    int id = config_id;
+    if (id < 0) {
+        id = select_config(M, N, K, ds->hw, ds->bpc, nullptr);
+        if (id < 0) return id;
+    }
+    Plan p;
+    st = make_plan(id, bcol, M, N, K, A, lda, B, ldb, const_cast<int32_t *>(C), ldc, ds->hw.num_cu, &p);
+    if (st != TDI8_OK) return st;
+    r.config_id = id;
+    r.form = p.form;
+    r.splits = p.g.splits;
+    r.kernels = p.zero_first ? 2 : 1;
+    r.grid_x = static_cast<int>(p.grid.x);
+    r.grid_y = static_cast<int>(p.grid.y);
+    r.threads = static_cast<int>(p.block.x);
+    *out = r;
     return TDI8_OK;
 }
 

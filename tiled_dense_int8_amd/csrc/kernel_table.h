@@ -42,6 +42,18 @@ struct KernelSet {
 constexpr int kRrGroupCols = 128;
 constexpr int rr_group_bk(int bm) { return bm == 16 ? 512 : 256; }
 
+// Resources of a configuration's column-major-B unpredicated kernel
+// (kernel[1][1], the one its occupancy is taken on), read by the build from
+// the AMDGPU metadata of the compiled code object: vector registers per lane
+// (the metadata's count, which on gfx950 spans both register files: the
+// architectural registers, rounded up to a multiple of 4, then the
+// accumulation registers), of which accumulation registers, scalar registers
+// per wave, static LDS per block and scratch per lane in bytes.
+struct KernelResources {
+    int unified_vgprs, agprs, sgprs, lds_bytes, scratch_bytes;
+};
+extern const KernelResources kKernelResources[TDI8_NUM_CONFIGS];
+
 // One registration function per configuration, each defined in its own
 // translation unit so the instantiations compile in parallel.
 #define TDI8_DECLARE_REGISTER(ID, ...) void register_cfg_##ID(KernelSet *ks);
