@@ -546,6 +546,88 @@ def trace_summary(trace_csv, plan_path):
     print_sweep_table(plan["sweep"], sw, info, rows, "rocprofv3 kernel-trace durations, mean of the timed dispatches")
 
 
+def ceilings():
+    """Practical ceilings of the operations the GEMM kernels are made of
+    (libtdi8_ceilings.so), printed as a markdown table: the int8 matrix-core
+    rate on random and on constant operands and the clock each runs at, the
+    HBM read rate of a plain 16 MiB read (the skinny workload's B) and of a
+    256 MiB one, 16-byte load rates from L2 at 16-byte alignment and
+    misaligned, and the duration of an empty grid of the skinny kernel's shape
+    (HIP events over back-to-back launches; the kernel-trace durations of the
+    same run are the profile)."""
+    import ctypes
+    import numpy as np
+    import torch
+    import synthetic
+    path = os.path.join(ROOT, "tiled_dense_int8_amd", "libtdi8_ceilings.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build it with tiled_dense_int8_amd/build.py")
+    lib = ctypes.CDLL(path)
+    p, i, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.tdi8c_mfma_loop.argtypes = [p, i, i, p, p, p]
+    lib.tdi8c_stream_read.argtypes = [p, i64, i, p, p]
+    lib.tdi8c_load16.argtypes = [p, i, i, i, p, p, p]
+    lib.tdi8c_empty.argtypes = [i, i, p]
+    sh = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+    cyc = torch.zeros(8192, dtype=torch.int64, device="cuda")
+
+    def timed(fn, reps):
+        assert fn() == 0
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3  # seconds per launch
+
+    rows = []
+    rnd = torch.from_numpy(synthetic.uniform_int8(16 * 256, 16, seed=0, tag=6)).cuda()
+    const = torch.ones(16 * 256 * 16, dtype=torch.int8, device="cuda")
+    iters = 20000
+    for name, ops in (("random int8 operands", rnd), ("constant operands (all 1)", const)):
+        s = timed(lambda: lib.tdi8c_mfma_loop(ops.data_ptr(), cus, iters, out.data_ptr(), cyc.data_ptr(), sh), 5)
+        ghz = cyc[:cus].double().mean().item() / s / 1e9
+        tops = cus * 4 * iters * 8 * 65536 / s / 1e12
+        rows.append((f"v_mfma_i32_32x32x32_i8 loop, {name}", f"{tops:.0f} TOP/s ({tops / MFMA_PEAK_TOPS:.3f} of 5.0 POP/s)",
+                     f"shader clock {ghz:.2f} GHz"))
+        log(f"[ceilings] mfma {name}: {tops:.0f} TOPS at {ghz:.2f} GHz")
+    for mib, nsets in ((16, 48), (256, 3)):
+        n = mib << 20
+        bufs = [torch.empty(n, dtype=torch.int8, device="cuda").random_(-128, 127) for _ in range(nsets)]
+        k = [0]
+
+        def read():
+            b = bufs[k[0] % nsets]
+            k[0] += 1
+            return lib.tdi8c_stream_read(b.data_ptr(), n, 4 * cus, out.data_ptr(), sh)
+        s = timed(read, 200 if mib == 16 else 20)
+        rows.append((f"plain read of {mib} MiB, 16-byte loads, {nsets} rotating buffers",
+                     f"{n / s / 1e9:.0f} GB/s ({n / s / 1e9 / HBM_PEAK_GBS:.3f} of 8 TB/s)", f"{s * 1e6:.2f} µs per launch"))
+        log(f"[ceilings] read {mib} MiB: {s * 1e6:.2f} us, {n / s / 1e9:.0f} GB/s")
+        del bufs
+        torch.cuda.empty_cache()
+    region = torch.ones((1 << 20) + 16, dtype=torch.int8, device="cuda")
+    for mis in (0, 8, 4, 1):
+        it = 2000
+        s = timed(lambda: lib.tdi8c_load16(region.data_ptr(), mis, cus, it, out.data_ptr(), cyc.data_ptr(), sh), 5)
+        c = cyc[:cus].double().mean().item()
+        per_cu = 512 * 16 * 8 * it / c
+        rows.append((f"16-byte loads from L2, {mis} bytes off 16-byte alignment", f"{per_cu:.1f} B/clk per CU",
+                     f"{cus * 512 * 16 * 8 * it / s / 1e12:.1f} TB/s"))
+        log(f"[ceilings] load16 misalign {mis}: {per_cu:.1f} B/clk/CU")
+    s = timed(lambda: lib.tdi8c_empty(cus, 1024, sh), 1000)
+    rows.append((f"empty grid, {cus} blocks of 1024 threads", f"{s * 1e6:.2f} µs per launch (back to back)", ""))
+    print("| ceiling | rate | note |")
+    print("|---|---|---|")
+    for r in rows:
+        print(f"| {r[0]} | {r[1]} | {r[2]} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -564,6 +646,9 @@ def main():
                     help="only time one forced configuration over a range of K and fit time = a + b K")
     ap.add_argument("--plan", default=None, help="with --sweep: write the launch plan here (JSON); "
                     "with --trace-summary: read it")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the practical ceilings (matrix-core rate, HBM read, aligned and misaligned "
+                         "loads, empty grid) with the calibration kernels")
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="only summarise a rocprofv3 kernel trace of a --sweep run (needs --plan)")
     args = ap.parse_args()
@@ -578,6 +663,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.ceilings:
+        ceilings()
+        return
     if args.calibrate_copy:
         n = args.calibrate_copy << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
@@ -670,6 +758,9 @@ def main():
                                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                                          "traffic": traffic_for("skinny16")},
                             "counters": counters_for("skinny16")}
+        if not args.no_cpu_baseline:
+            log("[bench] cpu baseline (oracle) for skinny16")
+            result["skinny"]["cpu_baseline"] = cpu_baseline(ws, sA, sB, budget_s=4.0)
         del ssets
 
     if not args.no_cpu_baseline:

@@ -1,0 +1,55 @@
+/*
+ * tdi8_ceilings.h -- roofline calibration kernels (libtdi8_ceilings.so), a
+ * measurement aid beside the GEMM library, used by bench.py --ceilings.
+ *
+ * The roofline the pages set out ("CUDA编程实践", section 3: compare a
+ * kernel's compute intensity with peak compute over memory bandwidth) is
+ * drawn here with the vendor's published peaks; these kernels measure what
+ * the same hardware reaches in practice for the operations the GEMM kernels
+ * are made of, so a kernel's distance from its roofline can be split into
+ * what the hardware allows and what the kernel loses.
+ *
+ * All pointers are device memory owned by the caller; every call is
+ * asynchronous on `stream` and returns 0, -1 (NULL pointer), -2 (invalid
+ * size) or -(hipError_t) of a failed launch.  `cycles` receives one 64-bit
+ * shader-clock count per block (s_memtime around the timed loop).
+ */
+#ifndef TDI8_CEILINGS_H
+#define TDI8_CEILINGS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+/* v_mfma_i32_32x32x32_i8 back to back, eight independent accumulators per
+ * wave, blocks of 256 threads (one wave per SIMD when one block per compute
+ * unit runs).  operands: 16 * 256 16-byte values (64 KiB) read once into
+ * registers; iters rounds of 8 instructions per wave; out: blocks * 256 int32
+ * (results, so the work is kept); cycles: blocks entries.  Work per call:
+ * blocks * 4 * iters * 8 * 65536 int8 operations. */
+int tdi8c_mfma_loop(const int8_t *operands, int blocks, int iters, int32_t *out, uint64_t *cycles,
+                    hipStream_t stream);
+
+/* Read `bytes` (a multiple of 16) at src with 16-byte loads, `blocks` blocks
+ * of 256 threads; out: one int32 (written only for an improbable value). */
+int tdi8c_stream_read(const int8_t *src, int64_t bytes, int blocks, int32_t *out, hipStream_t stream);
+
+/* 16-byte loads at region + misalign + 16 c over a 1 MiB region (c < 65536;
+ * the caller provides 1 MiB + 16 bytes), blocks of 512 threads, iters rounds
+ * of eight loads per lane; out: 512 int32; cycles: blocks entries.  Bytes
+ * read per call: blocks * 512 * 16 * 8 * iters. */
+int tdi8c_load16(const int8_t *region, int misalign, int blocks, int iters, int32_t *out, uint64_t *cycles,
+                 hipStream_t stream);
+
+/* A grid of blocks x threads that does nothing. */
+int tdi8c_empty(int blocks, int threads, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TDI8_CEILINGS_H */

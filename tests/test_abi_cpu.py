@@ -316,3 +316,21 @@ def test_torch_wrappers_refuse_host_tensors_and_bad_arguments():
         t.conv2d(x, w[..., :8].contiguous(), (1, 1))
     with pytest.raises(ValueError, match="contiguous"):
         t.conv2d(x.permute(0, 2, 1, 3), w, (1, 1))
+
+
+def test_ceilings_library_exports_its_header():
+    """The calibration library (bench.py --ceilings) loads and exports every
+    function its header declares; host-side argument checks need no device."""
+    path = os.path.join(os.path.dirname(t.LIB_PATH), "libtdi8_ceilings.so")
+    header = os.path.join(os.path.dirname(HEADER), "tdi8_ceilings.h")
+    text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^\s*int\s+(\w+)\s*\(", text, flags=re.M)))
+    assert names == ["tdi8c_empty", "tdi8c_load16", "tdi8c_mfma_loop", "tdi8c_stream_read"]
+    lib = ctypes.CDLL(path)
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.tdi8c_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.tdi8c_stream_read(None, 16, 1, None, None) == -1
+    assert lib.tdi8c_stream_read(A, 15, 1, C, None) == -2
+    lib.tdi8c_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert lib.tdi8c_empty(1, 2048, None) == -2

@@ -1,0 +1,132 @@
+// Roofline calibration kernels for gfx950 (measurement only; the GEMM
+// library does not use them).  Each measures one practical ceiling that the
+// GEMM kernels' roofline fractions are read against:
+//  * tdi8c_mfma_loop: v_mfma_i32_32x32x32_i8 back to back on register
+//    operands taken from a caller buffer, eight independent accumulators per
+//    wave, one wave per SIMD: the matrix-core rate for those operand bytes
+//    (random bytes switch more transistors than constant ones, and the clock
+//    follows the power drawn);
+//  * tdi8c_stream_read: a plain read of a buffer with 16-byte loads, the HBM
+//    read rate a kernel of that size reaches;
+//  * tdi8c_load16: 16-byte loads from a 1 MiB region that stays in L2, at a
+//    given byte offset from 16-byte alignment (rows of a tight odd leading
+//    dimension are misaligned);
+//  * tdi8c_empty: a launch that does nothing, the fixed cost of a grid.
+// Cycle counts come from s_memtime (the shader clock) per block.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/tdi8_ceilings.h"
+
+namespace {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+constexpr int kAcc = 8;
+
+// 256 threads (one wave per SIMD); operands: 2 * kAcc * 256 16-byte values.
+__global__ void __launch_bounds__(256) mfma_loop_kernel(const i32x4 *ops, int iters, int32_t *out,
+                                                        uint64_t *cycles) {
+    const int tid = threadIdx.x;
+    i32x4 a[kAcc], b[kAcc];
+#pragma unroll
+    for (int j = 0; j < kAcc; ++j) {
+        a[j] = ops[(2 * j) * 256 + tid];
+        b[j] = ops[(2 * j + 1) * 256 + tid];
+    }
+    i32x16 acc[kAcc];
+#pragma unroll
+    for (int j = 0; j < kAcc; ++j) acc[j] = i32x16{};
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < kAcc; ++j)
+            acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[j], b[(j + 1) % kAcc], acc[j], 0, 0, 0);
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    int32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < kAcc; ++j) s ^= acc[j][0] ^ acc[j][7] ^ acc[j][15];
+    out[blockIdx.x * 256 + tid] = s;
+    if (tid == 0) cycles[blockIdx.x] = t1 - t0;
+}
+
+// Every thread reads 16-byte chunks i, i + stride, ... (four in flight).
+__global__ void __launch_bounds__(256) stream_read_kernel(const i32x4 *src, int64_t chunks, int32_t *out) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    i32x4 acc = {0, 0, 0, 0};
+    int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    for (; i + 3 * stride < chunks; i += 4 * stride) {
+        const i32x4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+        acc ^= v0 ^ v1 ^ v2 ^ v3;
+    }
+    for (; i < chunks; i += stride) acc ^= src[i];
+    // written only for one improbable value, so the loads are kept and
+    // nothing is stored in practice
+    if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x5bd1e995) out[0] = 1;
+}
+
+// 512 threads; lane reads 16 bytes at base + misalign + 16 c, c inside the
+// 1 MiB region (65536 chunks), eight loads in flight per wave.
+__global__ void __launch_bounds__(512) load16_kernel(const int8_t *base, int misalign, int iters, int32_t *out,
+                                                     uint64_t *cycles) {
+    typedef i32x4 i32x4_u __attribute__((aligned(1)));
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    i32x4 acc = {0, 0, 0, 0};
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < iters; ++it) {
+        i32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int c = (static_cast<int>(blockIdx.x) * 977 + lane + 64 * (wave * 8 + u) + it * 4096) & 65535;
+            v[u] = *reinterpret_cast<const i32x4_u *>(base + misalign + 16 * static_cast<int64_t>(c));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u];
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x5bd1e995) out[tid] = 1;
+    if (tid == 0) cycles[blockIdx.x] = t1 - t0;
+}
+
+__global__ void empty_kernel() {}
+
+int status_of(hipError_t e) { return e == hipSuccess ? 0 : -static_cast<int>(e); }
+
+}  // namespace
+
+extern "C" {
+
+int tdi8c_mfma_loop(const int8_t *operands, int blocks, int iters, int32_t *out, uint64_t *cycles,
+                    hipStream_t stream) {
+    if (!operands || !out || !cycles) return -1;
+    if (blocks <= 0 || iters <= 0) return -2;
+    hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const i32x4 *>(operands), iters, out, cycles);
+    return status_of(hipGetLastError());
+}
+
+int tdi8c_stream_read(const int8_t *src, int64_t bytes, int blocks, int32_t *out, hipStream_t stream) {
+    if (!src || !out) return -1;
+    if (bytes < 16 || bytes % 16 != 0 || blocks <= 0) return -2;
+    hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, stream, reinterpret_cast<const i32x4 *>(src),
+                       bytes / 16, out);
+    return status_of(hipGetLastError());
+}
+
+int tdi8c_load16(const int8_t *region, int misalign, int blocks, int iters, int32_t *out, uint64_t *cycles,
+                 hipStream_t stream) {
+    if (!region || !out || !cycles) return -1;
+    if (misalign < 0 || misalign > 15 || blocks <= 0 || iters <= 0) return -2;
+    hipLaunchKernelGGL(load16_kernel, dim3(blocks), dim3(512), 0, stream, region, misalign, iters, out, cycles);
+    return status_of(hipGetLastError());
+}
+
+int tdi8c_empty(int blocks, int threads, hipStream_t stream) {
+    if (blocks <= 0 || threads <= 0 || threads > 1024) return -2;
+    hipLaunchKernelGGL(empty_kernel, dim3(blocks), dim3(threads), 0, stream);
+    return status_of(hipGetLastError());
+}
+
+}  // extern "C"
