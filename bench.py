@@ -13,7 +13,6 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -57,36 +56,37 @@ def log(msg: str) -> None:
     sys.stderr.flush()
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "tiled_dense_int8_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
-    return h.hexdigest()[:16]
+def kernel_code_hash() -> str:
+    """Identity of the GPU code in the built library (tdi8_kernel_code_hash:
+    SHA-256 of the gfx950 code objects); counter summaries record it, and
+    are used only while the library's kernels are the ones they measured."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "tiled_dense_int8_amd", "libtdi8.so"))
+    lib.tdi8_kernel_code_hash.restype = ctypes.c_char_p
+    return lib.tdi8_kernel_code_hash().decode()
 
 
 def traffic_for(workload: str):
     """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel sources; else None."""
+    taken on the kernels of the built library; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_code_hash") != kernel_code_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
 def counters_for(workload: str):
     """Matrix-core utilisation, clock and wait share of the workload's kernel
-    from the committed rocprofv3 --pmc summary, if it was taken on the current
-    kernel sources; else None."""
+    from the committed rocprofv3 --pmc summary, if it was taken on the kernels
+    of the built library; else None."""
     path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_code_hash") != kernel_code_hash():
         return None
     return {k: rec.get(k) for k in ("mfma_busy_frac", "clock_ghz", "waitcnt_wave_frac", "source")}
 
@@ -546,6 +546,124 @@ def trace_summary(trace_csv, plan_path):
     print_sweep_table(plan["sweep"], sw, info, rows, "rocprofv3 kernel-trace durations, mean of the timed dispatches")
 
 
+FORM_NAMES = {0: "none", 1: "predicated", 2: "pipelined", 3: "pipelined edge", 4: "split", 5: "split edge",
+              6: "skinny DMA", 7: "skinny predicated", 8: "skinny row groups", 9: "predicated prefetch"}
+
+
+def block_timelines(t, names, launches=20, warmup=300):
+    """Per-block timelines of each workload's product kernel, from the
+    instrumented build of the library (libtdi8_stamps.so: the same kernels,
+    each block recording its shader clock at entry, after its K loop and at
+    exit, the 100 MHz constant clock at entry and exit, and the compute unit
+    and XCD it ran on; include/tdi8_stamps.h).  Cold inputs rotating as in
+    the timed steps; `launches` launches each write their own record buffer,
+    enqueued behind a spin kernel so that they run back to back whatever the
+    host's submission rate.  Prints markdown: per workload the launch span,
+    the idle gap between consecutive launches, the shader clock the blocks
+    ran at, how a block's time splits between its K loop and what follows it
+    (the C epilogue), and for the headline workload the same per XCD."""
+    import ctypes
+    import numpy as np
+    import torch
+    path = os.path.join(ROOT, "tiled_dense_int8_amd", "libtdi8_stamps.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build it with tiled_dense_int8_amd/build.py")
+    lib = t.load_library(path)
+    lib.tdi8_stamps_set.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.tdi8_stamps_set.restype = ctypes.c_int
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    summary, per_xcd = [], []
+    for name in names:
+        w = WORKLOADS[name]
+        M, N, K = w["M"], w["N"], w["K"]
+        nsets = rotation_sets(w)
+        _, _, sets = make_sets(w, nsets)
+        fn = lib.gemm_s8s8s32_bt if w["bcm"] else lib.gemm_s8s8s32
+        args = [(M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0), c.data_ptr(), c.stride(0), sh)
+                for (a, b, c) in sets]
+        a, b, c = sets[0]
+        plan = t.gemm_plan(-1, w["bcm"], M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0),
+                           c.data_ptr(), c.stride(0))
+        blocks = plan.grid_x * plan.grid_y
+        recs = torch.zeros((launches, blocks, 8), dtype=torch.int64, device="cuda")
+        assert lib.tdi8_stamps_set(None, 0) == t.OK
+        for i in range(warmup):
+            assert fn(*args[i % nsets]) == t.OK
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(4_000_000)  # a few ms of spinning while the launches below queue up
+        e0.record(stream)
+        for i in range(launches):
+            assert lib.tdi8_stamps_set(recs[i].data_ptr(), blocks) == t.OK
+            assert fn(*args[i % nsets]) == t.OK
+        e1.record(stream)
+        torch.cuda.synchronize()
+        assert lib.tdi8_stamps_set(None, 0) == t.OK
+        event_us = e0.elapsed_time(e1) * 1e3 / launches
+        r = recs.cpu().numpy().astype(np.float64)
+        del sets, recs
+        torch.cuda.empty_cache()
+        c0, cm, c1, r0, r1 = r[..., 0], r[..., 1], r[..., 2], r[..., 3], r[..., 4]
+        ids = r[..., 5].astype(np.int64)
+        assert (r1 > r0).all() and (c1 > c0).all(), "every block wrote its record"
+        real_us = (r1 - r0) / 100.0                         # 100 MHz constant clock
+        ghz = (c1 - c0).sum() / (r1 - r0).sum() * 0.1      # shader cycles per 10 ns
+        span = (r1.max(axis=1) - r0.min(axis=1)) / 100.0
+        start_spread = (r0.max(axis=1) - r0.min(axis=1)) / 100.0
+        gap = (r0.min(axis=1)[1:] - r1.max(axis=1)[:-1]) / 100.0  # idle between consecutive launches
+        has_loop = (cm > 0).all()
+        loop_share = np.where(has_loop, (cm - c0) / (c1 - c0), np.nan)
+        after_us = np.where(has_loop, (c1 - cm) / (c1 - c0) * real_us, np.nan)
+        cu_key = (ids >> 32) * 256 + ((ids >> 8) & 0xFF)  # XCC, SE, SH, CU
+        cus = len(set(cu_key[0].tolist()))
+        # block time by how many blocks of the same launch ran on its compute unit
+        sharing = {}
+        for li in range(launches):
+            keys, counts = np.unique(cu_key[li], return_counts=True)
+            per = dict(zip(keys.tolist(), counts.tolist()))
+            for bi in range(blocks):
+                sharing.setdefault(per[int(cu_key[li, bi])], []).append(real_us[li, bi])
+        share_txt = ", ".join(f"{k}: {np.median(v):.2f} ({len(v) // launches})" for k, v in sorted(sharing.items()))
+        summary.append({
+            "workload": name, "config": plan.config_id, "form": FORM_NAMES.get(plan.form, str(plan.form)),
+            "blocks": blocks, "threads": plan.threads, "cus": cus, "event_us": event_us,
+            "span_us": float(np.median(span)), "gap_us": float(np.median(gap)), "ghz": float(ghz),
+            "block_med": float(np.median(real_us)), "block_max": float(np.median(real_us.max(axis=1))),
+            "loop_share": float(np.nanmedian(loop_share)) if has_loop else None,
+            "after_med": float(np.nanmedian(after_us)) if has_loop else None,
+            "after_max": float(np.median(np.nanmax(after_us, axis=1))) if has_loop else None,
+            "start_spread": float(np.median(start_spread)), "sharing": share_txt})
+        if name == names[0]:
+            xcc = ids >> 32
+            t0 = r0.min(axis=1, keepdims=True)
+            for x in sorted(set(xcc[0].tolist())):
+                sel = xcc == x
+                per_xcd.append((name, x, int(sel[0].sum()), float(np.median(real_us[sel])),
+                                float(np.median(np.where(sel, (r1 - t0) / 100.0, 0).max(axis=1))),
+                                float((c1 - c0)[sel].sum() / (r1 - r0)[sel].sum() * 0.1),
+                                float(np.nanmedian(loop_share[sel])) if has_loop else None))
+        log(f"[stamps] {name}: span {np.median(span):.2f} us, event {event_us:.2f} us, clock {ghz:.3f} GHz")
+    print("| workload | config, form | blocks x threads (CUs used) | µs per launch, back to back (events) | "
+          "span µs | gap to the next launch µs | shader clock GHz | block µs median / slowest | "
+          "K loop share of a block | after the loop µs median / slowest | start spread µs | "
+          "block µs median by blocks on its CU per launch (blocks) |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for x in summary:
+        loop = "-" if x["loop_share"] is None else f"{x['loop_share']:.3f}"
+        after = "-" if x["after_med"] is None else f"{x['after_med']:.2f} / {x['after_max']:.2f}"
+        print(f"| {x['workload']} | {x['config']}, {x['form']} | {x['blocks']} x {x['threads']} ({x['cus']}) | "
+              f"{x['event_us']:.2f} | {x['span_us']:.2f} | {x['gap_us']:.2f} | {x['ghz']:.3f} | {x['block_med']:.2f} / "
+              f"{x['block_max']:.2f} | {loop} | {after} | {x['start_spread']:.2f} | {x['sharing']} |")
+    if per_xcd:
+        print()
+        print(f"Per XCD ({per_xcd[0][0]}): | XCD | blocks | block µs median | last block ends at µs | "
+              "shader clock GHz | K loop share |")
+        print("|---|---|---|---|---|---|")
+        for (_, x, n, bm, end, g, ls) in per_xcd:
+            print(f"| {x} | {n} | {bm:.2f} | {end:.2f} | {g:.3f} | {'-' if ls is None else f'{ls:.3f}'} |")
+
+
 def ceilings():
     """Practical ceilings of the operations the GEMM kernels are made of
     (libtdi8_ceilings.so), printed as a markdown table: the int8 matrix-core
@@ -649,6 +767,9 @@ def main():
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure the practical ceilings (matrix-core rate, HBM read, aligned and misaligned "
                          "loads, empty grid) with the calibration kernels")
+    ap.add_argument("--stamps", action="store_true",
+                    help="only print per-block timelines (clock, K loop vs epilogue) of every workload's kernel "
+                         "from the instrumented build libtdi8_stamps.so")
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="only summarise a rocprofv3 kernel trace of a --sweep run (needs --plan)")
     args = ap.parse_args()
@@ -683,6 +804,10 @@ def main():
         return
     if args.sweep:
         k_sweep(t, args.sweep, args.plan)
+        return
+    if args.stamps:
+        first = args.workload if args.workload in WORKLOADS else "square4096"
+        block_timelines(t, [first] + [n for n in WORKLOADS if n != first])
         return
     if args.workload in CONV_WORKLOADS:
         print(json.dumps(conv_bench(t, args.workload, args.steps, args.warmup)), flush=True)

@@ -221,7 +221,9 @@ typedef enum {
     TDI8_FORM_SPLIT_EDGE = 5,       /* zero fill, then the K split of its edge form */
     TDI8_FORM_SKINNY_DMA = 6,       /* skinny kernel fed by LDS DMA (either B layout) */
     TDI8_FORM_SKINNY_PREDICATED = 7,/* skinny kernel with masked register loads */
-    TDI8_FORM_SKINNY_ROW_GROUPS = 8 /* zero fill, then the row-major-B column groups of a skinny tile */
+    TDI8_FORM_SKINNY_ROW_GROUPS = 8,/* zero fill, then the row-major-B column groups of a skinny tile */
+    TDI8_FORM_PREDICATED_PREFETCH = 9 /* the predicated kernel with two K tiles of loads in flight:
+                                       * column-major B, at most one block per compute unit */
 } tdi8_form;
 
 typedef struct {
@@ -322,6 +324,15 @@ const char *tdi8_status_string(int status);
  * the error those launch wrappers obtain from hipGetLastError, kept per
  * thread for the caller after an entry point returned TDI8_ERR_HIP. */
 int tdi8_last_hip_error(void);
+
+/* Identity of the GPU code compiled into this library: the first 16 hex
+ * digits of the SHA-256 of the gfx950 code objects of every configuration,
+ * in configuration order (static string; the caller must not free it).  Two
+ * builds report the same value exactly when their kernels are the same
+ * machine code, so a measurement taken on one build (a counter pass, a
+ * kernel trace) can record it and be matched against the library that runs
+ * later.  Not part of the pages' method: a build identity for measurements. */
+const char *tdi8_kernel_code_hash(void);
 
 #ifdef __cplusplus
 }

@@ -334,3 +334,21 @@ def test_ceilings_library_exports_its_header():
     assert lib.tdi8c_stream_read(A, 15, 1, C, None) == -2
     lib.tdi8c_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     assert lib.tdi8c_empty(1, 2048, None) == -2
+
+
+def test_stamps_library_exports_the_api_and_its_header():
+    """The instrumented build (bench.py --stamps) exports every function of
+    tdi8.h and of tdi8_stamps.h; the product library exports no stamp call."""
+    path = os.path.join(os.path.dirname(t.LIB_PATH), "libtdi8_stamps.so")
+    header = os.path.join(os.path.dirname(HEADER), "tdi8_stamps.h")
+    text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^\s*int\s+(\w+)\s*\(", text, flags=re.M)))
+    assert names == ["tdi8_stamps_set"]
+    lib = ctypes.CDLL(path)
+    for n in names + declared_functions():
+        assert hasattr(lib, n), n
+    assert not hasattr(ctypes.CDLL(t.LIB_PATH), "tdi8_stamps_set")
+    lib.tdi8_stamps_set.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    assert lib.tdi8_stamps_set(None, 4) == t.ERR_INVALID_VALUE
+    assert lib.tdi8_stamps_set(None, -1) == t.ERR_INVALID_VALUE
+    assert lib.tdi8_stamps_set(None, 0) == t.OK

@@ -587,3 +587,57 @@ def test_long_k_random(lib, bcm):
     for (M, N, K) in [(16, 256, 65536), (256, 256, 32768), (33, 70, 20000)]:
         A, B = synthetic.gemm_inputs(M, N, K, seed=5)
         check_case(DeviceCase(A, B, bcm), f"long K {M}x{N}x{K}")
+
+
+def prefetch_fits(c):
+    """The tile fits the deep-prefetch loop: whole 16-byte loads per thread,
+    at most four per thread and K tile for A and B together."""
+    a, b = c.block_m * c.block_k // 16, c.block_n * c.block_k // 16
+    return a % c.threads == 0 and b % c.threads == 0 and a // c.threads + b // c.threads <= 4
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_predicated_deep_prefetch_boundaries(lib, bcm):
+    """The predicated kernels (odd leading dimensions, misaligned pointers)
+    of every general configuration at K around the deep-prefetch loop's
+    bounds: fewer than three K tiles, a whole number of K tiles, one byte
+    more, several groups of tiles in flight, tails of 1 to 16 bytes, with
+    real bytes past K in every row and ragged M and N (edge rows read a
+    clamped row).  The deep loop runs for column-major B whenever the tile
+    fits it and the grid has at most one block per compute unit."""
+    t = lib
+    deep = 0
+    for c in table(t):
+        if c.family != 0:
+            continue
+        BK = c.block_k
+        ks = sorted({16, 2 * BK + 5, 3 * BK, 4 * BK, 4 * BK + 1, 5 * BK, 5 * BK + 9, 8 * BK + 15, 9 * BK + 16,
+                     17 * BK + 7})
+        for i, K in enumerate(ks):
+            M, N = c.block_m + 5 + i, 2 * c.block_n - 3
+            A, B = synthetic.gemm_inputs(M, N, K, seed=31 * c.id + i)
+            case = DeviceCase(A, B, bcm, lda=K + 1 + 2 * (i % 3), ldb=(K if bcm else N) + 3,
+                              offsets=(1 + i % 5, 3, 0))
+            p = plan_of(case, c.id)
+            want = bcm and prefetch_fits(c) and -(-K // BK) >= 3
+            assert p.form == (t.FORM_PREDICATED_PREFETCH if want else t.FORM_PREDICATED), (c.id, K, p.as_dict())
+            deep += want
+            check_case(case, f"predicated cfg{c.id} form {p.form}", config=c.id)
+    assert deep > 0 or not bcm
+
+
+def test_predicated_prefetch_only_for_small_grids(lib):
+    """The same K and configuration on a grid of at most one block per
+    compute unit (deep-prefetch loop) and on a larger one (the other loop):
+    both bit-exact."""
+    t = lib
+    c = table(t)[t.select_tile_config(1000, 3000, 777)]
+    assert prefetch_fits(c)
+    for (M, N) in [(600, 1000), (1000, 3000)]:
+        K = 777
+        A, B = synthetic.gemm_inputs(M, N, K, seed=M)
+        case = DeviceCase(A, B, True)
+        p = plan_of(case, c.id)
+        blocks = -(-M // c.block_m) * -(-N // c.block_n)
+        assert p.form == (t.FORM_PREDICATED_PREFETCH if blocks <= 256 else t.FORM_PREDICATED), p.as_dict()
+        check_case(case, f"predicated {M}x{N}x{K} form {p.form}", config=c.id)

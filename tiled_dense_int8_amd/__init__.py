@@ -54,7 +54,7 @@ class Selection(ctypes.Structure):
 
 
 FORM_NONE, FORM_PREDICATED, FORM_PIPELINED, FORM_PIPELINED_EDGE, FORM_SPLIT, FORM_SPLIT_EDGE, \
-    FORM_SKINNY_DMA, FORM_SKINNY_PREDICATED, FORM_SKINNY_ROW_GROUPS = range(9)
+    FORM_SKINNY_DMA, FORM_SKINNY_PREDICATED, FORM_SKINNY_ROW_GROUPS, FORM_PREDICATED_PREFETCH = range(10)
 
 
 class Plan(ctypes.Structure):
@@ -86,6 +86,7 @@ _SIGNATURES = {
     "conv2d_validate": (_i, [_i] * 13 + [_p, _p, _p]),
     "tdi8_status_string": (ctypes.c_char_p, [_i]),
     "tdi8_last_hip_error": (_i, []),
+    "tdi8_kernel_code_hash": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGNATURES.items():
     _f = getattr(_lib, _name)
@@ -93,6 +94,18 @@ for _name, (_res, _args) in _SIGNATURES.items():
     _f.argtypes = _args
 
 EXPORTED = tuple(_SIGNATURES)
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Another build of the same C ABI (the instrumented libtdi8_stamps.so),
+    loaded beside libtdi8.so with the same signatures; its functions take the
+    arguments of the module-level ones of the same name."""
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
 
 
 class TDI8Error(RuntimeError):
@@ -188,6 +201,10 @@ def tdi8_status_string(status: int) -> str:
 
 def tdi8_last_hip_error() -> int:
     return _lib.tdi8_last_hip_error()
+
+
+def tdi8_kernel_code_hash() -> str:
+    return _lib.tdi8_kernel_code_hash().decode()
 
 
 # ----- torch convenience -----------------------------------------------------------

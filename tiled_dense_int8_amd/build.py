@@ -8,11 +8,18 @@ Between compiling and linking, the register and LDS use of every
 configuration's column-major kernel (the one the selection's occupancy is
 taken on) is read from the AMDGPU metadata note of the gfx950 code object
 this build just produced, and compiled into the library as a table
-(_build/kernel_resources.cpp): tile_config_info reports it.
+(_build/kernel_resources.cpp): tile_config_info reports it.  The same file
+carries the SHA-256 of those code objects (tdi8_kernel_code_hash).
+
+The library build also produces libtdi8_ceilings.so (roofline calibration
+kernels) and libtdi8_stamps.so: the same sources compiled with TDI8_STAMPS,
+whose kernels write per-block timelines (include/tdi8_stamps.h); its
+objects go to _build/stamps/.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import re
 import subprocess
@@ -27,6 +34,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtdi8.so")
 CEILINGS_LIB = os.path.join(PKG, "libtdi8_ceilings.so")  # roofline calibration kernels (bench.py --ceilings)
+STAMPS_LIB = os.path.join(PKG, "libtdi8_stamps.so")      # block timelines (bench.py --stamps)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 LLVM_BIN = "/opt/rocm/llvm/bin"
 ARCH = "gfx950"
@@ -73,11 +81,16 @@ def occupancy_kernel_symbol(params: tuple[int, ...]) -> str:
     return f"_ZN4tdi822gemm_skinny_lds_kernelI{args}EEvNS_8GemmArgsE"
 
 
+def code_object_path(obj: str, work: str) -> str:
+    return os.path.join(work, os.path.basename(obj) + ".co")
+
+
 def code_object_kernels(obj: str, work: str) -> dict[str, dict]:
     """Kernel name -> metadata (.vgpr_count, .agpr_count, ...) of the gfx950
-    code object embedded in a host object built here."""
+    code object embedded in a host object built here (the code object is left
+    at code_object_path(obj, work))."""
     fatbin = os.path.join(work, os.path.basename(obj) + ".fatbin")
-    co = os.path.join(work, os.path.basename(obj) + ".co")
+    co = code_object_path(obj, work)
     _run([os.path.join(LLVM_BIN, "llvm-objcopy"), f"--dump-section=.hip_fatbin={fatbin}", obj,
           os.path.join(work, os.path.basename(obj) + ".stripped")])
     _run([os.path.join(LLVM_BIN, "clang-offload-bundler"), "--unbundle", "--type=o",
@@ -93,12 +106,15 @@ def write_resource_table(objs: dict[int, str], bdir: str) -> str:
     """Generate the C++ table of per-configuration kernel resources."""
     params = config_params()
     rows = []
+    code = hashlib.sha256()
     for cid in sorted(params):
         kernels = code_object_kernels(objs[cid], bdir)
         sym = occupancy_kernel_symbol(params[cid])
         if sym not in kernels:
             raise RuntimeError(f"configuration {cid}: kernel {sym} not found in {objs[cid]}")
         k = kernels[sym]
+        with open(code_object_path(objs[cid], bdir), "rb") as f:
+            code.update(f.read())
         rows.append(f"    {{{k['.vgpr_count']}, {k['.agpr_count']}, {k['.sgpr_count']}, "
                     f"{k['.group_segment_fixed_size']}, {k['.private_segment_fixed_size']}}},  // {cid}")
     src = os.path.join(bdir, "kernel_resources.cpp")
@@ -107,7 +123,9 @@ def write_resource_table(objs: dict[int, str], bdir: str) -> str:
             "// column-major-B unpredicated kernel.\n"
             '#include "kernel_table.h"\n\nnamespace tdi8 {\n\n'
             "const KernelResources kKernelResources[TDI8_NUM_CONFIGS] = {\n" + "\n".join(rows) +
-            "\n};\n\n}  // namespace tdi8\n")
+            "\n};\n\n}  // namespace tdi8\n\n"
+            "// SHA-256 of the code objects of every configuration, in id order.\n"
+            'extern "C" const char *tdi8_kernel_code_hash(void) { return "' + code.hexdigest()[:16] + '"; }\n')
     with open(src, "w") as f:
         f.write(text)
     return src
@@ -133,7 +151,7 @@ def build(jobs: int | None = None, verbose: bool = False, extra_flags: list[str]
     ceil_obj = os.path.join(bdir, "ceilings.o")
     ceil_unit = [HIPCC, *flags, "-c", os.path.join(CSRC, "ceilings.hip"), "-o", ceil_obj]
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        list(ex.map(_run, units + [ceil_unit]))
+        list(ex.map(_run, units + ([ceil_unit] if out == LIB else [])))
     objs = [u[u.index("-o") + 1] for u in units]
     res_src = write_resource_table({cid: os.path.join(bdir, f"cfg{cid}.o") for cid in config_ids()}, bdir)
     res_obj = os.path.join(bdir, "kernel_resources.o")
@@ -146,6 +164,7 @@ def build(jobs: int | None = None, verbose: bool = False, extra_flags: list[str]
         tmp = CEILINGS_LIB + ".tmp%d" % os.getpid()
         _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", ceil_obj, "-o", tmp])
         os.replace(tmp, CEILINGS_LIB)
+        build(jobs, verbose, list(extra_flags or []) + ["-DTDI8_STAMPS"], STAMPS_LIB, os.path.join(bdir, "stamps"))
     if verbose:
         print("built", out)
     return out

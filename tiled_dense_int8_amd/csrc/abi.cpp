@@ -10,6 +10,9 @@
 #include <mutex>
 
 #include "../../include/tdi8.h"
+#if defined(TDI8_STAMPS)
+#include "../../include/tdi8_stamps.h"
+#endif
 #include "kernel_table.h"
 #include "selector.h"
 #include "device_common.h"
@@ -43,6 +46,18 @@ int hip_fail(hipError_t e) {
     g_last_hip_error = static_cast<int>(e);
     return TDI8_ERR_HIP;
 }
+
+#if defined(TDI8_STAMPS)
+// Timeline buffer of the instrumented library (tdi8_stamps_set).
+uint64_t *g_stamps = nullptr;
+int g_stamp_cap = 0;
+void attach_stamps(GemmArgs &g) {
+    g.stamps = g_stamps;
+    g.stamp_cap = g_stamp_cap;
+}
+#else
+void attach_stamps(GemmArgs &) {}
+#endif
 
 const KernelSet *kernels() {
     static const KernelSet *table = [] {
@@ -175,6 +190,18 @@ int make_plan(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, c
             p->form = !fast ? TDI8_FORM_PREDICATED : edge ? TDI8_FORM_PIPELINED_EDGE : TDI8_FORM_PIPELINED;
             p->kernel = edge ? kernels()[id].edge[b] : kernels()[id].kernel[b][fast ? 1 : 0];
             p->grid = dim3(static_cast<unsigned>(tm * tn));
+            // The predicated kernel with two K tiles of loads in flight pays
+            // when each compute unit holds at most one block, whose loop is
+            // then latency-bound (1000 x 1000 x 8191: 80.8 -> 49.9 us); with
+            // more blocks per unit, whose loads already keep its
+            // misaligned-load path busy, it cost 3-13% (1000 x 3000 x 777:
+            // 12.2 -> 13.8 us).  It needs column-major B, K >= 16 and
+            // three K tiles.
+            if (!fast && bcol && kernels()[id].prefetch && tm * tn <= num_cu && K >= 16 &&
+                (K + c.bk - 1) / c.bk >= 3) {
+                p->form = TDI8_FORM_PREDICATED_PREFETCH;
+                p->kernel = kernels()[id].prefetch;
+            }
         }
         return TDI8_OK;
     }
@@ -222,6 +249,7 @@ int make_plan(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, c
 // Enqueue a plan: for a K split, first the fill kernel that zeroes the C
 // window, whose blocks then add their partial sums into it.
 int run_plan(Plan &p, hipStream_t stream) {
+    attach_stamps(p.g);
     void *args[] = {&p.g};
     hipError_t e;
     if (p.zero_first) {
@@ -343,6 +371,7 @@ int conv_entry(int cfg, const ConvShape &c, const int8_t *x, const int8_t *w, in
             g.K = static_cast<int>(c.R * runp * 16);
         }
     }
+    attach_stamps(g);
     void *args[] = {&g, &cv};
     hipError_t e = hipLaunchKernel(dma ? kernels()[id].conv : kernels()[id].conv_gather,
                                    dim3(static_cast<unsigned>(tm * tn)), dim3(sc.threads), args, 0, stream);
@@ -548,5 +577,14 @@ const char *tdi8_status_string(int status) {
 }
 
 int tdi8_last_hip_error(void) { return g_last_hip_error; }
+
+#if defined(TDI8_STAMPS)
+int tdi8_stamps_set(uint64_t *records, int capacity) {
+    if (capacity < 0 || (capacity > 0 && records == nullptr)) return TDI8_ERR_INVALID_VALUE;
+    g_stamps = capacity > 0 ? records : nullptr;
+    g_stamp_cap = capacity;
+    return TDI8_OK;
+}
+#endif
 
 }  // extern "C"

@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace tdi8 {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -19,6 +22,10 @@ struct GemmArgs {
     int M, N, K;
     int tiles_m, tiles_n;  // block tiles along M and N
     int splits;            // K slices (1: each block covers all of K)
+#if defined(TDI8_STAMPS)
+    uint64_t *stamps;      // timeline records (BlockStamp), one per block id below stamp_cap
+    int stamp_cap;
+#endif
 };
 
 // Convolution geometry (NHWC image, KRSC filters): image N x H x W x C,
@@ -57,6 +64,35 @@ __device__ __forceinline__ int fast_div(int n, FastDiv f) {
     return static_cast<int>((__umulhi(nn, f.magic) + nn) >> f.shift);
 }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+#define TDI8_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14))
+// s_waitcnt lgkmcnt(0) with the other counters left at max.
+#define TDI8_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (3 << 14))
+
+// Block barrier that waits on no memory counter (callers first wait for
+// exactly what they need; __syncthreads() also waits for every outstanding
+// global load) and that the compiler may not move memory accesses across:
+// the barrier builtin alone is not a memory operation to the optimiser, the
+// empty asm statements with a memory clobber are.
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1 in order: loop bodies
+// that index register arrays by a compile-time value.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ int clamp16(int v) { return v < 0 ? 0 : (v > 16 ? 16 : v); }
 __device__ __forceinline__ int clamp4(int v) { return v < 0 ? 0 : (v > 4 ? 4 : v); }
 
@@ -81,6 +117,18 @@ __device__ __forceinline__ i32x4 shift_up_bytes(i32x4 v, int n) {
         nlo = lo << b;
         nhi = b == 0 ? hi : (hi << b) | (lo >> (64 - b));
     }
+    return i32x4{static_cast<int32_t>(static_cast<uint32_t>(nlo)), static_cast<int32_t>(nlo >> 32),
+                 static_cast<int32_t>(static_cast<uint32_t>(nhi)), static_cast<int32_t>(nhi >> 32)};
+}
+
+// v with every byte moved down by n bytes (byte i + n to i, zeros above;
+// 0 <= n <= 16, so n = 16 gives zero).
+__device__ __forceinline__ i32x4 shift_down_bytes(i32x4 v, int n) {
+    const uint64_t lo = static_cast<uint32_t>(v[0]) | (static_cast<uint64_t>(static_cast<uint32_t>(v[1])) << 32);
+    const uint64_t hi = static_cast<uint32_t>(v[2]) | (static_cast<uint64_t>(static_cast<uint32_t>(v[3])) << 32);
+    const int b = 8 * n;
+    const uint64_t nhi = b >= 64 ? 0 : hi >> b;
+    const uint64_t nlo = b >= 128 ? 0 : b >= 64 ? hi >> (b - 64) : b == 0 ? lo : (lo >> b) | (hi << (64 - b));
     return i32x4{static_cast<int32_t>(static_cast<uint32_t>(nlo)), static_cast<int32_t>(nlo >> 32),
                  static_cast<int32_t>(static_cast<uint32_t>(nhi)), static_cast<int32_t>(nhi >> 32)};
 }
@@ -180,5 +228,47 @@ __device__ __forceinline__ void store4_nt(const GemmArgs &g, int m, int n, i32x4
     }
     __builtin_nontemporal_store(v, reinterpret_cast<i32x4_a4 *>(g.C + static_cast<int64_t>(m) * g.ldc + n));
 }
+
+// Block timeline, compiled only into the instrumented library
+// (libtdi8_stamps.so, built with -DTDI8_STAMPS; the GEMM library's kernels do
+// not contain it).  Per block: the shader clock (s_memtime) at entry, when
+// the K loop is done and at exit, the constant 100 MHz clock (s_memrealtime)
+// at entry and exit, and the hardware ids (HW_ID, XCC_ID) of the compute
+// unit that ran it.  The clocks sit in scalar registers until the block
+// ends; lane 0 of the block then writes one 64-byte record with vector
+// stores, so nothing inside the timed stretch waits on memory for them.
+struct BlockStamp {
+#if defined(TDI8_STAMPS) && defined(__HIP_DEVICE_COMPILE__)
+    uint64_t c0 = 0, cm = 0, r0 = 0;
+    __device__ __forceinline__ void begin() {
+        c0 = __builtin_amdgcn_s_memtime();
+        r0 = __builtin_amdgcn_s_memrealtime();
+    }
+    __device__ __forceinline__ void loop_done() { cm = __builtin_amdgcn_s_memtime(); }
+    __device__ __forceinline__ void end(const GemmArgs &g) {
+        const uint64_t c1 = __builtin_amdgcn_s_memtime();
+        const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+        uint32_t hw, xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        const int64_t b = blockIdx.x + static_cast<int64_t>(blockIdx.y) * gridDim.x;
+        if (threadIdx.x == 0 && g.stamps != nullptr && b < g.stamp_cap) {
+            uint64_t *r = g.stamps + 8 * b;
+            r[0] = c0;
+            r[1] = cm;
+            r[2] = c1;
+            r[3] = r0;
+            r[4] = r1;
+            r[5] = (static_cast<uint64_t>(xcc) << 32) | hw;
+            r[6] = static_cast<uint64_t>(b);
+            r[7] = 0;
+        }
+    }
+#else
+    __device__ __forceinline__ void begin() {}
+    __device__ __forceinline__ void loop_done() {}
+    __device__ __forceinline__ void end(const GemmArgs &) {}
+#endif
+};
 
 }  // namespace tdi8

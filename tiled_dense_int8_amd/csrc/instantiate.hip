@@ -77,6 +77,17 @@ static const void *split_edge_entry() {
         return nullptr;
 }
 
+// The predicated column-major-B kernel with the deep-prefetch loop, for
+// tiles that fit it.
+template <class P>
+static const void *prefetch_entry() {
+    if constexpr (P::family == 0 &&
+                  deep_prefetch_fits(P::wm * P::mf * P::mt, P::wn * P::mf * P::nt, P::bk, P::wm * P::wn * 64))
+        return reinterpret_cast<const void *>(&gemm_tiled_prefetch_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk>);
+    else
+        return nullptr;
+}
+
 template <class P>
 static const void *conv_entry() {
     if constexpr (P::family == 0)
@@ -116,6 +127,7 @@ void TDI8_CAT(register_cfg_, TDI8_CFG)(KernelSet *ks) {
     ks->kernel[0][1] = entry<P, false, true>();
     ks->kernel[1][0] = entry<P, true, false>();
     ks->kernel[1][1] = entry<P, true, true>();
+    ks->prefetch = prefetch_entry<P>();
     ks->split[0] = split_entry<P, false>();
     ks->split[1] = split_entry<P, true>();
     ks->edge[0] = edge_entry<P, false>();

@@ -22,10 +22,13 @@ TDI8_CONFIG_LIST(TDI8_DEFINE_PARAMS)
 // general kernel for whole tiles); split[b_col_major]: its K-split form,
 // edge[b_col_major]: its form for sizes that end inside a tile and
 // split_edge[b_col_major]: the K split of that form, whose slices may end
-// inside a K tile (null for the skinny family); conv: the implicit-GEMM
+// inside a K tile (null for the skinny family); prefetch: the predicated
+// column-major-B kernel with the deep-prefetch K loop (null where the tile
+// does not fit it, and for the skinny family); conv: the implicit-GEMM
 // convolution form.
 struct KernelSet {
     const void *kernel[2][2];
+    const void *prefetch;
     const void *split[2];
     const void *edge[2];
     const void *split_edge[2];

@@ -38,23 +38,6 @@ namespace tdi8 {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
-#define TDI8_WAIT_VMCNT(n) \
-    __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14))
-// s_waitcnt lgkmcnt(0) with the other counters left at max.
-#define TDI8_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (3 << 14))
-
-// Block barrier that waits on no memory counter (callers first wait for
-// exactly what they need) and that the compiler may not move memory accesses
-// across: the barrier builtin alone is not a memory operation to the
-// optimiser, the empty asm statements with a memory clobber are.
-__device__ __forceinline__ void block_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // Sixteen zero bytes in device memory: the DMA source of chunks that lie
 // outside the operand (zero padding of the convolution, K and row tails).
 static __device__ __attribute__((aligned(16))) const int8_t zero_chunk[16] = {};
@@ -119,6 +102,8 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
 
     __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * STAGE];
+    BlockStamp stamp;
+    stamp.begin();
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -449,6 +434,7 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
         for (; t + 1 < nk; ++t) tile(t, T0{}, T1{}, T0{});
         tile(t, T0{}, T0{}, T0{});
     }
+    stamp.loop_done();
 
     if constexpr (SPLIT) {
         // Partial sums go through LDS (free once the K loop is done), so that
@@ -494,6 +480,7 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
                     atomicAdd(g.C + static_cast<int64_t>(m0 + p0 + r) * g.ldc + n0 + c, cl[r * RS + c]);
             }
         }
+        stamp.end(g);
         return;
     }
 
@@ -559,6 +546,7 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
             }
         }
     }
+    stamp.end(g);
 #endif
 }
 

@@ -47,6 +47,8 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_kernel(GemmArgs g) {
     constexpr int TILES = MT * NT;
 
     __shared__ i32x4 red[WK][TILES][64];
+    BlockStamp stamp;
+    stamp.begin();
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -117,6 +119,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_kernel(GemmArgs g) {
                     for (int j = 0; j < NT; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[u][j][q], xa[u][i][q], acc[i][j], 0, 0, 0);
     }
+    stamp.loop_done();
 
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -136,6 +139,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_kernel(GemmArgs g) {
         const int n = n0 + 16 * (tile % NT) + 4 * (l >> 4);
         store4<FAST>(g, m, n, sum);
     }
+    stamp.end(g);
 }
 
 // Unpredicated skinny kernel for column-major B (used when K % KC == 0 and
@@ -171,6 +175,8 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
     // Block sum, accumulated with LDS atomics; element e of lane l at
     // [tile][e][l], so the 64 lanes of one atomic hit 64 different banks.
     __shared__ int32_t red[TILES][4][64];
+    BlockStamp stamp;
+    stamp.begin();
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -250,6 +256,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
             issue(c + 2);
         }
     }
+    stamp.loop_done();
 
     // Sum the waves' partial tiles: integer addition is exact in any order,
     // so every wave adds its tile into one LDS copy with atomics.
@@ -269,6 +276,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
         const int n = n0 + 16 * (tile % NT) + 4 * (l >> 4);
         if (m < g.M) store4<true>(g, m, n, sum);
     }
+    stamp.end(g);
 #endif
 }
 
@@ -309,6 +317,8 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
 #if defined(__HIP_DEVICE_COMPILE__)
     __shared__ __attribute__((aligned(1024))) int8_t buf[2][STAGE];
     __shared__ int32_t red[TILES][4][64];   // as in gemm_skinny_lds_kernel
+    BlockStamp stamp;
+    stamp.begin();
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -407,6 +417,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
             issue(c + 2);
         }
     }
+    stamp.loop_done();
 
     __syncthreads();
 #pragma unroll
@@ -424,6 +435,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
         const int n = n0 + 16 * (tile % NT) + 4 * (l >> 4);
         if (m < g.M) store4<true>(g, m, n, sum);
     }
+    stamp.end(g);
 #endif
 }
 
@@ -433,6 +445,8 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rr_kernel(GemmArgs g) {
     constexpr int BN = 64;
 
     __shared__ i32x4 red[WK][MT * 4][64];
+    BlockStamp stamp;
+    stamp.begin();
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -494,6 +508,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rr_kernel(GemmArgs g) {
                     acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j], xa[u][i], acc[i][j], 0, 0, 0);
         }
     }
+    stamp.loop_done();
 
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -520,6 +535,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rr_kernel(GemmArgs g) {
         const int n = n0 + 4 * (4 * (l >> 4) + e);
         store4<FAST>(g, m, n, v);
     }
+    stamp.end(g);
 }
 
 }  // namespace tdi8

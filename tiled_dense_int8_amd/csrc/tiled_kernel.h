@@ -174,7 +174,18 @@ __device__ __forceinline__ i32x4 conv_run16(const int8_t *img, int ih0, int iw0,
 // SRC 0: the product of the operands described by g.  SRC 1: implicit-GEMM
 // convolution (A rows gathered from the NHWC image by conv_gather16, B the
 // KRSC filters as column-major K x R S C, C the N P Q x K output).
-template <int MF, int WM, int WN, int MT, int NT, int BK, bool BCOL, bool FAST, int SRC>
+// Whether a tile can take the deep-prefetch loop: A and B tiles split into
+// whole 16-byte loads per thread, at most four per thread and K tile (a
+// larger set would not fit the register budget of the tile's occupancy).
+constexpr bool deep_prefetch_fits(int bm, int bn, int bk, int threads) {
+    return (bm * bk / 16) % threads == 0 && (bn * bk / 16) % threads == 0 &&
+           (bm * bk / 16) / threads + (bn * bk / 16) / threads <= 4;
+}
+
+// DEEP: the K loop with two register sets of loads in flight (below); the
+// dispatcher runs it for column-major B when the grid holds at most one
+// block per compute unit, K >= 16 and there are at least three K tiles.
+template <int MF, int WM, int WN, int MT, int NT, int BK, bool BCOL, bool FAST, int SRC, bool DEEP = false>
 __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &cv) {
     static_assert(SRC == 0 || (BCOL && !FAST), "the gathered convolution is the predicated column-major form");
     constexpr int NTH = WM * WN * 64;
@@ -193,6 +204,8 @@ __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &
     using Acc = typename Mfma<MF>::Acc;
 
     __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
+    BlockStamp stamp;
+    stamp.begin();
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -350,7 +363,135 @@ __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &
     };
 
     const int nk = (g.K + BK - 1) / BK;
-    if (nk > 0) {
+    if constexpr (DEEP) {
+        static_assert(SRC == 0 && !FAST && BCOL && deep_prefetch_fits(BM, BN, BK, NTH),
+                      "deep prefetch: column-major B, whole load sets of at most four loads per thread");
+        // Deep prefetch (K >= 16, column-major B): PD register sets hold the
+        // K tiles in flight, so a tile's loads are issued PD iterations
+        // before it is stashed instead of one (PD = 2: of 2, 3 and 4 sets,
+        // two were fastest on 512 x 512 x 4097, 2000 x 2000 x 2001 and
+        // 1000 x 3000 x 777, where two blocks per compute unit already
+        // load at the rate of its misaligned 16-byte loads).  Every set is filled by the
+        // same unconditional 16-byte loads, whatever the tile (a fixed load
+        // count per set keeps the compiler's waits counting only the set
+        // being stashed), from addresses that are always inside the
+        // operands:
+        //  * rows past M or N read row M-1 or N-1: they only reach C rows or
+        //    columns past M or N, which are never stored;
+        //  * in the last K tile, when K is not a multiple of BK, a chunk
+        //    that ends past K is read from the row's last 16 bytes,
+        //    [K-16, K), and moved down to its place at the stash, the bytes
+        //    past K becoming zero (shift_down_bytes); a chunk wholly past K
+        //    reads the row's first 16 bytes and becomes zero.
+        // The barrier between K tiles waits on LDS only (block_barrier):
+        // __syncthreads() would also wait for the loads still in flight.
+        constexpr int PD = 2;
+        // the dispatcher guarantees both (a launch without them would
+        // leave C as it was)
+        if (g.K >= 16 && nk >= PD + 1) {
+            const int nfull = g.K / BK;  // K tiles wholly inside K; tile nfull (if any) is the tail
+            const int8_t *arow[A_PER];
+            const int8_t *brow[B_PER];
+            int acol[A_PER], bcol[B_PER];
+#pragma unroll
+            for (int i = 0; i < A_PER; ++i) {
+                const int q = tid + i * NTH;
+                const int r = q / CPR;
+                acol[i] = 16 * ((q % CPR) ^ chunk_swizzle<CPR>(r));
+                const int row = m0 + r < g.M ? m0 + r : g.M - 1;
+                arow[i] = g.A + static_cast<int64_t>(row) * g.lda;
+            }
+#pragma unroll
+            for (int i = 0; i < B_PER; ++i) {
+                const int q = tid + i * NTH;
+                const int r = q / CPR;
+                bcol[i] = 16 * ((q % CPR) ^ chunk_swizzle<CPR>(r));
+                const int col = n0 + r < g.N ? n0 + r : g.N - 1;
+                brow[i] = g.B + static_cast<int64_t>(col) * g.ldb;
+            }
+            i32x4 qa[PD][A_PER], qb[PD][B_PER];
+            int tsa[A_PER] = {}, tsb[B_PER] = {};  // tail tile: bytes to move each chunk down (16: zero)
+            // Row offset of the chunk at kk: in place, except in the tail
+            // tile, where a chunk ending past K reads [K-16, K) and one
+            // wholly past K reads [0, 16), then moves down by 16 - nv bytes
+            // (nv valid bytes stay, the rest becomes zero).  Tiles j >= nk
+            // (the loop runs whole groups of PD iterations) read the
+            // operands' first 16 bytes: the same loads, one cache line per
+            // instruction, never stashed.  The choices are selects on
+            // uniform values, with the loads after them: branches around
+            // the address arithmetic let the compiler move the loads into
+            // the branches, and its waits then count none of them.
+            auto pick = [&](const int8_t *row, const int8_t *dummy, int kk, bool tail, bool live, int &shift) {
+                const int nv = clamp16(g.K - kk);
+                const int toff = nv == 16 ? kk : (nv > 0 ? g.K - 16 : 0);
+                shift = tail ? 16 - nv : shift;
+                const int8_t *p = row + (tail ? toff : kk);
+                return live ? p : dummy;
+            };
+            auto fetch_deep = [&](int j, i32x4 (&xa)[A_PER], i32x4 (&xb)[B_PER]) {
+                const int k0 = j * BK;
+                const bool tail = j == nfull;
+                const bool live = j < nk;
+                const int8_t *pa[A_PER];
+                const int8_t *pb[B_PER];
+#pragma unroll
+                for (int i = 0; i < A_PER; ++i) pa[i] = pick(arow[i], g.A, k0 + acol[i], tail, live, tsa[i]);
+#pragma unroll
+                for (int i = 0; i < B_PER; ++i) pb[i] = pick(brow[i], g.B, k0 + bcol[i], tail, live, tsb[i]);
+#pragma unroll
+                for (int i = 0; i < A_PER; ++i) xa[i] = load16_unaligned(pa[i]);
+#pragma unroll
+                for (int i = 0; i < B_PER; ++i) xb[i] = load16_unaligned(pb[i]);
+            };
+            auto stash_deep = [&](int j, const i32x4 (&xa)[A_PER], const i32x4 (&xb)[B_PER]) {
+                int8_t *base = lds + (j & 1) * STAGE;
+                if (j == nfull) {
+#pragma unroll
+                    for (int i = 0; i < A_PER; ++i)
+                        *reinterpret_cast<i32x4 *>(base + 16 * (tid + i * NTH)) = shift_down_bytes(xa[i], tsa[i]);
+#pragma unroll
+                    for (int i = 0; i < B_PER; ++i)
+                        *reinterpret_cast<i32x4 *>(base + A_BYTES + 16 * (tid + i * NTH)) =
+                            shift_down_bytes(xb[i], tsb[i]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < A_PER; ++i) *reinterpret_cast<i32x4 *>(base + 16 * (tid + i * NTH)) = xa[i];
+#pragma unroll
+                    for (int i = 0; i < B_PER; ++i)
+                        *reinterpret_cast<i32x4 *>(base + A_BYTES + 16 * (tid + i * NTH)) = xb[i];
+                }
+            };
+            // Tile j lives in set j % PD.  Prologue: tiles 0 .. PD-1 in
+            // flight, tile 0 stashed and its set refilled with tile PD.
+            static_for<PD>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                fetch_deep(u, qa[u], qb[u]);
+            });
+            stash_deep(0, qa[0], qb[0]);
+            fetch_deep(PD, qa[0], qb[0]);
+            TDI8_WAIT_LGKM0();
+            block_barrier();
+            // Iteration t: tile t's matrix work, tile t+1 to the other LDS
+            // stage, its set refilled with tile t+1+PD, one barrier on LDS
+            // only.  Whole groups of PD iterations, so that set indices are
+            // compile-time and every iteration issues the same loads; the
+            // iterations past the last tile only load (uniform branches
+            // around LDS and matrix work leave the load sequence fixed).
+            const int groups = (nk + PD - 1) / PD;
+            for (int t0 = 0; t0 < groups * PD; t0 += PD) {
+                static_for<PD>([&](auto uc) {
+                    constexpr int U = (decltype(uc)::value + 1) % PD;
+                    const int t = t0 + decltype(uc)::value;
+                    if (t < nk) compute(t & 1);
+                    if (t + 1 < nk) stash_deep(t + 1, qa[U], qb[U]);
+                    fetch_deep(t + 1 + PD, qa[U], qb[U]);
+                    TDI8_WAIT_LGKM0();
+                    block_barrier();
+                });
+            }
+        }
+    }
+    if (!DEEP && nk > 0) {
         fetch(0);
         stash(0);
         __syncthreads();
@@ -361,6 +502,7 @@ __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &
             __syncthreads();
         }
     }
+    stamp.loop_done();
 
     // Epilogue: lane holds D[n][m] = C[m][n] with four consecutive n per
     // group of four accumulator registers.  32x32 tiles go through the LDS
@@ -409,11 +551,18 @@ __device__ __forceinline__ void tiled_body(const GemmArgs &g, const ConvParams &
             }
         }
     }
+    stamp.end(g);
 }
 
 template <int MF, int WM, int WN, int MT, int NT, int BK, bool BCOL, bool FAST>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_kernel(GemmArgs g) {
     tiled_body<MF, WM, WN, MT, NT, BK, BCOL, FAST, 0>(g, ConvParams{});
+}
+
+// The predicated column-major-B kernel with the deep-prefetch K loop.
+template <int MF, int WM, int WN, int MT, int NT, int BK>
+__global__ void __launch_bounds__(WM * WN * 64) gemm_tiled_prefetch_kernel(GemmArgs g) {
+    tiled_body<MF, WM, WN, MT, NT, BK, true, false, 0, true>(g, ConvParams{});
 }
 
 // Implicit-GEMM convolution for any channel count and alignment: the
