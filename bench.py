@@ -277,7 +277,7 @@ REGRET_SHAPES = [(256, 256, 256), (4096, 4096, 4096), (16, 4096, 4096), (1000, 3
                  (16384, 16384, 8192), (2048, 2048, 2048), (8192, 8192, 4096), (1024, 1024, 8192),
                  (256, 256, 32768), (512, 4096, 4096), (32, 4096, 4096), (16, 8192, 8192),
                  (4096, 16, 4096), (333, 777, 999), (1, 4096, 4096), (64, 4096, 4096), (128, 4096, 4096),
-                 (4096, 64, 4096), (64, 14336, 4096)]
+                 (4096, 64, 4096), (64, 14336, 4096), (1000, 1000, 8191), (512, 512, 4097)]
 
 
 PRUNE_THRESHOLD = 0.85
@@ -561,7 +561,10 @@ def block_timelines(t, names, launches=20, warmup=300):
     host's submission rate.  Prints markdown: per workload the launch span,
     the idle gap between consecutive launches, the shader clock the blocks
     ran at, how a block's time splits between its K loop and what follows it
-    (the C epilogue), and for the headline workload the same per XCD."""
+    (the C epilogue), block time by how many blocks share a compute unit,
+    the turnover from one block to the next on a compute unit that runs
+    them in turn (what a persistent tile loop would remove), and for the
+    headline workload the same per XCD."""
     import ctypes
     import numpy as np
     import torch
@@ -625,6 +628,16 @@ def block_timelines(t, names, launches=20, warmup=300):
             for bi in range(blocks):
                 sharing.setdefault(per[int(cu_key[li, bi])], []).append(real_us[li, bi])
         share_txt = ", ".join(f"{k}: {np.median(v):.2f} ({len(v) // launches})" for k, v in sorted(sharing.items()))
+        # turnover: on a compute unit that runs blocks one after another, the
+        # idle time from one block's end to the next one's start
+        turn = []
+        for li in range(launches):
+            for key in set(cu_key[li].tolist()):
+                sel = np.nonzero(cu_key[li] == key)[0]
+                order = sel[np.argsort(r0[li, sel])]
+                for a, b in zip(order[:-1], order[1:]):
+                    if r0[li, b] >= r1[li, a]:
+                        turn.append((r0[li, b] - r1[li, a]) / 100.0)
         summary.append({
             "workload": name, "config": plan.config_id, "form": FORM_NAMES.get(plan.form, str(plan.form)),
             "blocks": blocks, "threads": plan.threads, "cus": cus, "event_us": event_us,
@@ -633,7 +646,8 @@ def block_timelines(t, names, launches=20, warmup=300):
             "loop_share": float(np.nanmedian(loop_share)) if has_loop else None,
             "after_med": float(np.nanmedian(after_us)) if has_loop else None,
             "after_max": float(np.median(np.nanmax(after_us, axis=1))) if has_loop else None,
-            "start_spread": float(np.median(start_spread)), "sharing": share_txt})
+            "start_spread": float(np.median(start_spread)), "sharing": share_txt,
+            "turnover": (f"{np.median(turn):.2f} ({len(turn) // launches})" if turn else "-")})
         if name == names[0]:
             xcc = ids >> 32
             t0 = r0.min(axis=1, keepdims=True)
@@ -647,14 +661,14 @@ def block_timelines(t, names, launches=20, warmup=300):
     print("| workload | config, form | blocks x threads (CUs used) | µs per launch, back to back (events) | "
           "span µs | gap to the next launch µs | shader clock GHz | block µs median / slowest | "
           "K loop share of a block | after the loop µs median / slowest | start spread µs | "
-          "block µs median by blocks on its CU per launch (blocks) |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+          "block µs median by blocks on its CU per launch (blocks) | turnover µs median (block pairs) |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for x in summary:
         loop = "-" if x["loop_share"] is None else f"{x['loop_share']:.3f}"
         after = "-" if x["after_med"] is None else f"{x['after_med']:.2f} / {x['after_max']:.2f}"
         print(f"| {x['workload']} | {x['config']}, {x['form']} | {x['blocks']} x {x['threads']} ({x['cus']}) | "
               f"{x['event_us']:.2f} | {x['span_us']:.2f} | {x['gap_us']:.2f} | {x['ghz']:.3f} | {x['block_med']:.2f} / "
-              f"{x['block_max']:.2f} | {loop} | {after} | {x['start_spread']:.2f} | {x['sharing']} |")
+              f"{x['block_max']:.2f} | {loop} | {after} | {x['start_spread']:.2f} | {x['sharing']} | {x['turnover']} |")
     if per_xcd:
         print()
         print(f"Per XCD ({per_xcd[0][0]}): | XCD | blocks | block µs median | last block ends at µs | "
@@ -668,10 +682,11 @@ def ceilings():
     """Practical ceilings of the operations the GEMM kernels are made of
     (libtdi8_ceilings.so), printed as a markdown table: the int8 matrix-core
     rate on random and on constant operands and the clock each runs at, the
-    HBM read rate of a plain 16 MiB read (the skinny workload's B) and of a
-    256 MiB one, 16-byte load rates from L2 at 16-byte alignment and
-    misaligned, and the duration of an empty grid of the skinny kernel's shape
-    (HIP events over back-to-back launches; the kernel-trace durations of the
+    HBM read rate of a plain 16 MiB read (the skinny workload's B), of the
+    same bytes moved into LDS by DMA in per-block slabs (the skinny kernel's
+    B stream), and of a 256 MiB read, 16-byte load rates from L2 at 16-byte
+    alignment and misaligned, and the duration of an empty grid (HIP events
+    over launches queued back to back; the kernel-trace durations of the
     same run are the profile)."""
     import ctypes
     import numpy as np
@@ -686,6 +701,7 @@ def ceilings():
     lib.tdi8c_stream_read.argtypes = [p, i64, i, p, p]
     lib.tdi8c_load16.argtypes = [p, i, i, i, p, p, p]
     lib.tdi8c_empty.argtypes = [i, i, p]
+    lib.tdi8c_dma_read.argtypes = [p, i64, i, i, i, p, p]
     sh = torch.cuda.current_stream().cuda_stream
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
@@ -696,6 +712,7 @@ def ceilings():
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(3_000_000)  # the launches below queue up behind it and run back to back
         e0.record()
         for _ in range(reps):
             fn()
@@ -727,6 +744,18 @@ def ceilings():
         rows.append((f"plain read of {mib} MiB, 16-byte loads, {nsets} rotating buffers",
                      f"{n / s / 1e9:.0f} GB/s ({n / s / 1e9 / HBM_PEAK_GBS:.3f} of 8 TB/s)", f"{s * 1e6:.2f} µs per launch"))
         log(f"[ceilings] read {mib} MiB: {s * 1e6:.2f} us, {n / s / 1e9:.0f} GB/s")
+        if mib == 16:
+            for nt in (1, 0):
+                def dma():
+                    b = bufs[k[0] % nsets]
+                    k[0] += 1
+                    return lib.tdi8c_dma_read(b.data_ptr(), n, cus, 256, nt, out.data_ptr(), sh)
+                s = timed(dma, 200)
+                hint = "non-temporal hint" if nt else "no hint"
+                rows.append((f"LDS DMA read of 16 MiB, {cus} blocks of 256 threads, 64 KiB slabs, {hint}",
+                             f"{n / s / 1e9:.0f} GB/s ({n / s / 1e9 / HBM_PEAK_GBS:.3f} of 8 TB/s)",
+                             f"{s * 1e6:.2f} µs per launch"))
+                log(f"[ceilings] dma read 16 MiB nt={nt}: {s * 1e6:.2f} us")
         del bufs
         torch.cuda.empty_cache()
     region = torch.ones((1 << 20) + 16, dtype=torch.int8, device="cuda")
@@ -738,8 +767,9 @@ def ceilings():
         rows.append((f"16-byte loads from L2, {mis} bytes off 16-byte alignment", f"{per_cu:.1f} B/clk per CU",
                      f"{cus * 512 * 16 * 8 * it / s / 1e12:.1f} TB/s"))
         log(f"[ceilings] load16 misalign {mis}: {per_cu:.1f} B/clk/CU")
-    s = timed(lambda: lib.tdi8c_empty(cus, 1024, sh), 1000)
-    rows.append((f"empty grid, {cus} blocks of 1024 threads", f"{s * 1e6:.2f} µs per launch (back to back)", ""))
+    for threads in (1024, 256):
+        s = timed(lambda: lib.tdi8c_empty(cus, threads, sh), 1000)
+        rows.append((f"empty grid, {cus} blocks of {threads} threads", f"{s * 1e6:.2f} µs per launch (back to back)", ""))
     print("| ceiling | rate | note |")
     print("|---|---|---|")
     for r in rows:

@@ -38,6 +38,15 @@ int tdi8c_mfma_loop(const int8_t *operands, int blocks, int iters, int32_t *out,
  * of 256 threads; out: one int32 (written only for an improbable value). */
 int tdi8c_stream_read(const int8_t *src, int64_t bytes, int blocks, int32_t *out, hipStream_t stream);
 
+/* Move `bytes` at src into LDS with global_load_lds_dwordx4: block b takes
+ * the contiguous slab [b s, (b + 1) s), s = bytes / blocks (a multiple of
+ * 1 KiB, at most 64 KiB), in 1 KiB wave pieces, every load issued before one
+ * wait; threads a multiple of 64 up to 1024; nontemporal != 0 sets the
+ * non-temporal cache policy on the loads (the skinny kernel's B stream).
+ * out: one int32 (written only for an improbable value). */
+int tdi8c_dma_read(const int8_t *src, int64_t bytes, int blocks, int threads, int nontemporal, int32_t *out,
+                   hipStream_t stream);
+
 /* 16-byte loads at region + misalign + 16 c over a 1 MiB region (c < 65536;
  * the caller provides 1 MiB + 16 bytes), blocks of 512 threads, iters rounds
  * of eight loads per lane; out: 512 int32; cycles: blocks entries.  Bytes

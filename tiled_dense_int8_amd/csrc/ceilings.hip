@@ -8,6 +8,9 @@
 //    follows the power drawn);
 //  * tdi8c_stream_read: a plain read of a buffer with 16-byte loads, the HBM
 //    read rate a kernel of that size reaches;
+//  * tdi8c_dma_read: the same bytes moved into LDS by global_load_lds_dwordx4
+//    in per-block contiguous slabs, every load issued before the one wait
+//    (the skinny kernel's B stream without its A, matrix work and epilogue);
 //  * tdi8c_load16: 16-byte loads from a 1 MiB region that stays in L2, at a
 //    given byte offset from 16-byte alignment (rows of a tight odd leading
 //    dimension are misaligned);
@@ -90,6 +93,24 @@ __global__ void __launch_bounds__(512) load16_kernel(const int8_t *base, int mis
     if (tid == 0) cycles[blockIdx.x] = t1 - t0;
 }
 
+// Block b moves bytes [b slab, (b + 1) slab) into LDS in 1 KiB wave pieces
+// (slab a multiple of 1 KiB, at most 64 KiB); AUX: cache policy of the loads.
+template <int AUX>
+__global__ void __launch_bounds__(1024) dma_read_kernel(const int8_t *src, int64_t slab, int32_t *out) {
+    __shared__ __attribute__((aligned(1024))) int8_t buf[65536];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int8_t *p = src + static_cast<int64_t>(blockIdx.x) * slab;
+    const int pieces = static_cast<int>(slab >> 10);
+    for (int pc = wave; pc < pieces; pc += nw)
+        __builtin_amdgcn_global_load_lds(p + pc * 1024 + lane * 16,
+                                         (__attribute__((address_space(3))) void *)(buf + pc * 1024), 16, 0, AUX);
+    __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));  // vmcnt(0)
+    __syncthreads();
+    // written only for one improbable byte pattern, so the loads are kept
+    const int t = (threadIdx.x * 16) & 65535;
+    if (buf[t] == 0x7b && buf[t + 1] == 0x11 && buf[t + 2] == 0x13) out[0] = 1;
+}
+
 __global__ void empty_kernel() {}
 
 int status_of(hipError_t e) { return e == hipSuccess ? 0 : -static_cast<int>(e); }
@@ -112,6 +133,20 @@ int tdi8c_stream_read(const int8_t *src, int64_t bytes, int blocks, int32_t *out
     if (bytes < 16 || bytes % 16 != 0 || blocks <= 0) return -2;
     hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, stream, reinterpret_cast<const i32x4 *>(src),
                        bytes / 16, out);
+    return status_of(hipGetLastError());
+}
+
+int tdi8c_dma_read(const int8_t *src, int64_t bytes, int blocks, int threads, int nontemporal, int32_t *out,
+                   hipStream_t stream) {
+    if (!src || !out) return -1;
+    if (blocks <= 0 || threads < 64 || threads > 1024 || threads % 64 != 0 || bytes <= 0 || bytes % blocks != 0)
+        return -2;
+    const int64_t slab = bytes / blocks;
+    if (slab % 1024 != 0 || slab > 65536) return -2;
+    if (nontemporal)
+        hipLaunchKernelGGL(dma_read_kernel<2>, dim3(blocks), dim3(threads), 0, stream, src, slab, out);
+    else
+        hipLaunchKernelGGL(dma_read_kernel<0>, dim3(blocks), dim3(threads), 0, stream, src, slab, out);
     return status_of(hipGetLastError());
 }
 
