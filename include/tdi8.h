@@ -78,7 +78,13 @@ typedef enum {
 
 /* C = A x B, A row-major M x K, B row-major K x N, C row-major M x N.
  * M == 0 or N == 0: nothing is enqueued.  K == 0: the C window is set to 0.
- * Returns TDI8_OK or a negative tdi8_status. */
+ * The configuration is select_tile_config's, with one exception: when the
+ * operands take the predicated kernels (see above) with column-major B and
+ * the selected tiles number fewer than the compute units, the reuse-1
+ * configuration with the most tiles, at most one per compute unit, runs
+ * instead (the selection relies on the K split to fill the compute units,
+ * which the predicated kernels do not have; gemm_plan reports the one that
+ * runs).  Returns TDI8_OK or a negative tdi8_status. */
 int gemm_s8s8s32(int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
                  int32_t *C, int ldc, hipStream_t stream);
 

@@ -224,6 +224,33 @@ def split_k(c: Cfg, m: int, n: int, k: int, num_cu: int) -> int:
     return best
 
 
+def predicated_fill(c: Cfg, m: int, n: int, num_cu: int, table: list[Cfg]) -> Cfg:
+    """Configuration that runs a selected general configuration c when the
+    call takes the predicated form with column-major B (operands that the
+    16-byte DMA loads cannot move).  CDNA4 RULE, NOT A STEP OF THE CLAIMS
+    (parity unpinned against the pages): the selection counts on split_k to
+    fill the compute units when its tiles are few, and the predicated
+    kernels cannot split K.  Reading: when c's tiles (partial ones at the
+    ends of M and N counted) are fewer than num_cu, take among the reuse-1
+    general configurations (m_tiles = n_tiles = 1) with at most num_cu tiles
+    the one with the most tiles, ties to the deeper K tile, then table
+    order; c itself if none has more tiles than c."""
+    def tiles(x: Cfg) -> int:
+        return -(-m // x.BM) * -(-n // x.BN)
+    if c.family != "general" or tiles(c) >= num_cu:
+        return c
+    best = c
+    for x in table:
+        if x.family != "general" or x.m_tiles != 1 or x.n_tiles != 1 or x.excluded:
+            continue
+        t = tiles(x)
+        if t > num_cu:
+            continue
+        if t > tiles(best) or (t == tiles(best) and best is not c and x.block_k > best.block_k):
+            best = x
+    return best
+
+
 def no_overhang(cands: list[Cfg], m: int, n: int, table: list[Cfg]) -> list[Cfg]:
     """CDNA4 RULE, NOT A STEP OF THE CLAIMS (parity unpinned against the
     pages), added to step 1: keep the configurations whose block tile is

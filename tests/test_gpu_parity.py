@@ -461,6 +461,37 @@ def test_plan_of_the_workloads(lib):
         assert p.config_id == t.select_tile_config(M, N, K) and p.form == form, (M, N, K, bcm, p.as_dict())
 
 
+def test_predicated_fill_plan(lib):
+    """Calls whose operands take the predicated kernels with column-major B
+    run the configuration the oracle's predicated_fill gives for the
+    selection's pick (more tiles when the pick leaves compute units idle),
+    gemm_plan reports it, row-major B and forced ids are left alone, and the
+    results are bit-exact."""
+    from oracle.selector import Cfg, predicated_fill
+    t = lib
+    tab = table(t)
+    fam = {0: "general", 1: "skinny"}
+    otab = [Cfg(c.id, fam[c.family], c.mfma_m, c.mfma_n, c.waves_m, c.waves_n, c.m_tiles, c.n_tiles,
+                c.block_k, c.threads, c.blocks_per_cu, c.stages, bool(c.excluded)) for c in tab]
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    moved = 0
+    for (M, N, K) in [(1000, 1000, 8191), (512, 512, 4097), (333, 777, 999), (1000, 3000, 777), (900, 900, 1001),
+                      (40, 700, 300)]:
+        A, B = synthetic.gemm_inputs(M, N, K, seed=M + N)
+        sel = t.select_tile_config(M, N, K)
+        for bcm in (True, False):
+            case = DeviceCase(A, B, bcm, lda=K + 1, ldb=(K if bcm else N) + 1)
+            p = plan_of(case)
+            want = predicated_fill(otab[sel], M, N, cus, otab).id if (bcm and tab[sel].family == 0) else sel
+            assert p.config_id == want, (M, N, K, bcm, sel, p.as_dict())
+            assert plan_of(case, sel).config_id == sel
+            moved += want != sel
+            if M * N * K <= 1000 * 1000 * 8191 // 4 or want != sel:
+                check_case(case, f"predicated fill {M}x{N}x{K} bcm={bcm} cfg{p.config_id}")
+    assert moved >= 3
+
+
 # ---- the five workloads -------------------------------------------------------------
 
 def sampled_check(C_dev, A_store, B_store, bcm, M, N, K, seed, n_random=4096, freivalds=2):

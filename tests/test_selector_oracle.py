@@ -156,6 +156,46 @@ def test_split_k_worked_examples():
     assert split_k(g64x128, 256, 256, 32768, 120) == 8
 
 
+def test_predicated_fill_worked_examples():
+    """The predicated-form fill rule (a CDNA4 addition after the five steps),
+    worked by hand: when the selected tiles number fewer than the compute
+    units, the reuse-1 general configuration with the most tiles, at most
+    one per compute unit, runs instead; ties to the deeper K tile, then
+    table order; the selected one stays if no such configuration has more
+    tiles.  Tiles count the partial ones at the ends of M and N."""
+    from oracle.selector import predicated_fill
+    g = "general"
+    g64x128 = Cfg(7, g, 32, 32, 2, 4, 1, 1, 128, 512, 2)    # 64 x 128, BK 128
+    g128x64 = Cfg(9, g, 32, 32, 4, 2, 1, 1, 128, 512, 2)    # 128 x 64, BK 128
+    g64x64a = Cfg(5, g, 32, 32, 2, 2, 1, 1, 64, 256, 4)     # 64 x 64, BK 64
+    g64x64b = Cfg(11, g, 32, 32, 2, 2, 1, 1, 128, 256, 4)   # 64 x 64, BK 128
+    g256 = Cfg(0, g, 32, 32, 2, 4, 4, 2, 128, 512, 1)       # 256 x 256
+    sk = Cfg(12, "skinny", 16, 16, 1, 1, 1, 1, 2048, 1024, 1)
+    tab = [g256, g64x64a, g64x128, g128x64, g64x64b, sk]
+    # 1000 x 1000: 64 x 128 -> 16 * 8 = 128 tiles < 256; 64 x 64 -> 16 * 16 = 256 (both BK);
+    # 128 x 64 -> 8 * 16 = 128: the 64 x 64 pair ties at 256, the deeper K tile wins
+    assert predicated_fill(g64x128, 1000, 1000, 256, tab) is g64x64b
+    # 512 x 512: 8 * 4 = 32 tiles; 64 x 64 -> 64
+    assert predicated_fill(g64x128, 512, 512, 256, tab) is g64x64b
+    # 333 x 777: 6 * 7 = 42 tiles; 64 x 64 -> 6 * 13 = 78; 128 x 64 -> 3 * 13 = 39
+    assert predicated_fill(g64x128, 333, 777, 256, tab) is g64x64b
+    # 1000 x 3000: 16 * 24 = 384 >= 256 tiles: the selected configuration stays
+    assert predicated_fill(g64x128, 1000, 3000, 256, tab) is g64x128
+    # 1000 x 2000: 16 * 16 = 256: stays (no idle compute unit)
+    assert predicated_fill(g64x128, 1000, 2000, 256, tab) is g64x128
+    # 1500 x 1500 with 256 x 256 selected: 6 * 6 = 36 tiles; 64 x 64 -> 24 * 24 = 576 > 256 and
+    # 64 x 128 -> 24 * 12 = 288 > 256 are too many; 128 x 64 -> 12 * 24 = 288 too: none fits, it stays
+    assert predicated_fill(g256, 1500, 1500, 256, tab) is g256
+    # 900 x 900 with 256 x 256 selected: 4 * 4 = 16; 64 x 64 -> 15 * 15 = 225 <= 256
+    assert predicated_fill(g256, 900, 900, 256, tab) is g64x64b
+    # 120 compute units: 512 x 512 -> 64 x 64 gives 64 tiles <= 120
+    assert predicated_fill(g64x128, 512, 512, 120, tab) is g64x64b
+    # a tie in tiles with the selected one is no gain: 128 x 64 at 1000 x 1000 (128 tiles) keeps 64 x 128
+    assert predicated_fill(g64x128, 1000, 1000, 256, [g64x128, g128x64]) is g64x128
+    # the skinny family is never moved
+    assert predicated_fill(sk, 16, 100, 256, tab) is sk
+
+
 def test_claim3_excluded_reuse_scheme():
     """Claim 3's second alternative drops a reuse scheme at step 2.  Scheme
     4 x 4 of the fake table is id0 (256 x 256) and id4 (128 x 128, 16x16

@@ -241,4 +241,23 @@ int split_k_for(const StaticCfg &c, int M, int N, int K, int num_cu) {
     return s;
 }
 
+int predicated_fill(int id, int M, int N, int num_cu) {
+    const StaticCfg c = static_cfg(id);
+    auto tiles = [&](const StaticCfg &x) { return cdiv(M, x.bm) * cdiv(N, x.bn); };
+    if (c.family != 0 || tiles(c) >= num_cu) return id;
+    int best = id;
+    int64_t best_t = tiles(c);
+    for (int j = 0; j < TDI8_NUM_CONFIGS; ++j) {
+        const StaticCfg x = static_cfg(j);
+        if (x.family != 0 || x.mt != 1 || x.nt != 1 || x.excluded) continue;
+        const int64_t t = tiles(x);
+        if (t > num_cu) continue;
+        if (t > best_t || (t == best_t && best != id && x.bk > static_cfg(best).bk)) {
+            best = j;
+            best_t = t;
+        }
+    }
+    return best;
+}
+
 }  // namespace tdi8

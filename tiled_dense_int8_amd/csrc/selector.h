@@ -18,6 +18,15 @@ struct StaticCfg {
 
 StaticCfg static_cfg(int id);
 
+// Configuration that runs a selected general configuration when the call
+// takes the predicated form with column-major B: the selection counts on the
+// K split to fill the compute units when its tiles are few, which the
+// predicated kernels cannot do, so when the selected tiles number fewer than
+// num_cu, the reuse-1 general configuration with the most tiles (at most
+// num_cu; ties to the deeper K tile, then table order) runs instead, if it
+// has more tiles.  A CDNA4 rule after the five steps, not one of them.
+int predicated_fill(int id, int M, int N, int num_cu);
+
 // The selection on described hardware; bpc[id] = resident blocks per compute
 // unit of configuration id.  Returns the id, or a negative status.
 int select_config(int M, int N, int K, const tdi8_hw_info &hw, const int *bpc, tdi8_selection *out);
