@@ -310,8 +310,9 @@ def reuse_pruning(times_by_test, table, theta=PRUNE_THRESHOLD):
 def selector_report(t):
     """Time every applicable compiled configuration on a suite of shapes (both
     B layouts, inputs rotating as in the headline timing), and compare the
-    selection's pick with the fastest.  Every configuration's C must equal
-    the pick's byte for byte.  Prints a markdown table."""
+    configuration a call runs (the selection's pick, or where the predicated
+    form's fill rule moves it) with the fastest.  Every configuration's C
+    must equal the run one's byte for byte.  Prints a markdown table."""
     import torch
     torch.manual_seed(0)
     sh = torch.cuda.current_stream().cuda_stream
@@ -320,7 +321,7 @@ def selector_report(t):
     hw = t.HwInfo(props.multi_processor_count, 1024, 256, 32)
     routes = {t.ROUTE_GENERAL: "", t.ROUTE_FALLBACK: " reuse-1", t.ROUTE_SKINNY: " skinny"}
     times_by_test = {}
-    print("| M×N×K | B | selected (route) | selected µs | fastest | fastest µs | regret | configs timed |")
+    print("| M×N×K | B | selected (route) → run | run µs | fastest | fastest µs | regret | configs timed |")
     print("|---|---|---|---|---|---|---|---|")
     for (M, N, K) in REGRET_SHAPES:
         pick = t.select_tile_config(M, N, K)
@@ -333,8 +334,13 @@ def selector_report(t):
                      torch.randint(-128, 128, (N, K) if bcm else (K, N), dtype=torch.int8, device="cuda"),
                      torch.empty((M, N), dtype=torch.int32, device="cuda")) for _ in range(nsets)]
             cands = [c for c in table if c.family == 0 or M <= c.block_m or N <= c.block_n]
+            # the configuration the call runs: the selection's, or the one the
+            # predicated form's fill rule moves it to (gemm_plan)
+            a0, b0, c0 = sets[0]
+            run = t.gemm_plan(-1, bcm, M, N, K, a0.data_ptr(), a0.stride(0), b0.data_ptr(), b0.stride(0),
+                              c0.data_ptr(), c0.stride(0)).config_id
             times, ref = {}, None
-            for c in [table[pick]] + [c for c in cands if c.id != pick]:
+            for c in [table[run]] + [c for c in cands if c.id != run]:
                 args = [(c.id, int(bcm), M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0),
                          cc.data_ptr(), cc.stride(0), sh) for (a, b, cc) in sets]
                 t0 = time.perf_counter(); i = 0
@@ -357,12 +363,13 @@ def selector_report(t):
                 if ref is None:
                     ref = sets[0][2].clone()
                 else:
-                    assert torch.equal(sets[0][2], ref), f"config {c.id} differs from config {pick} at {M}x{N}x{K}"
+                    assert torch.equal(sets[0][2], ref), f"config {c.id} differs from config {run} at {M}x{N}x{K}"
             times_by_test[(M, N, K, bcm)] = times
             best = min(times, key=times.get)
             route = routes.get(sel.route, "")
-            print(f"| {M}×{N}×{K} | {'col' if bcm else 'row'} | {pick}{route} | {times[pick]:.2f} | {best} | "
-                  f"{times[best]:.2f} | {100.0 * (times[pick] / times[best] - 1):.0f}% | {len(times)} |", flush=True)
+            moved = "" if run == pick else f" → {run} (fill)"
+            print(f"| {M}×{N}×{K} | {'col' if bcm else 'row'} | {pick}{route}{moved} | {times[run]:.2f} | {best} | "
+                  f"{times[best]:.2f} | {100.0 * (times[run] / times[best] - 1):.0f}% | {len(times)} |", flush=True)
             del sets, ref
             torch.cuda.empty_cache()
     # claim 3's performance test over the same shapes and layouts
