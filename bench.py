@@ -709,6 +709,8 @@ def ceilings():
     lib.tdi8c_load16.argtypes = [p, i, i, i, p, p, p]
     lib.tdi8c_empty.argtypes = [i, i, p]
     lib.tdi8c_dma_read.argtypes = [p, i64, i, i, i, p, p]
+    lib.tdi8c_loop_mix.argtypes = [p, i, i, i, p, p, p]
+    lib.tdi8c_store_tiles.argtypes = [p, i, i, i64, i, p]
     sh = torch.cuda.current_stream().cuda_stream
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
@@ -777,6 +779,42 @@ def ceilings():
     for threads in (1024, 256):
         s = timed(lambda: lib.tdi8c_empty(cus, threads, sh), 1000)
         rows.append((f"empty grid, {cus} blocks of {threads} threads", f"{s * 1e6:.2f} µs per launch (back to back)", ""))
+    # the 256 x 256 configuration's K-tile operations, together and apart
+    src = torch.from_numpy(synthetic.uniform_int8(1 << 20, 1, seed=0, tag=7).reshape(-1)).cuda()
+    parts = {1: "LDS reads", 2: "LDS DMA", 4: "matrix instructions"}
+    for mode in (4, 1, 2, 3, 5, 6, 7):
+        it = 2000
+        s = timed(lambda: lib.tdi8c_loop_mix(src.data_ptr(), mode, cus, it, out.data_ptr(), cyc.data_ptr(), sh), 5)
+        c = cyc[:cus].double().mean().item()
+        ghz = c / s / 1e9
+        name = " + ".join(v for k, v in parts.items() if mode & k)
+        rate = []
+        if mode & 4:
+            tops = cus * it * 256 * 65536 / s / 1e12
+            rate.append(f"{tops:.0f} TOP/s ({tops / MFMA_PEAK_TOPS:.3f} of 5.0 POP/s), matrix cores "
+                        f"{it * 256 / 4 * 32 / c:.2f} busy")
+        if mode & 1:
+            rate.append(f"reads {it * 192 * 1024 / c:.0f} B/clk per CU")
+        if mode & 2:
+            rate.append(f"DMA {it * 64 * 1024 / c:.0f} B/clk per CU")
+        rows.append((f"256 x 256 K-tile mix: {name} (8 waves per CU, random bytes)", "; ".join(rate),
+                     f"shader clock {ghz:.2f} GHz"))
+        log(f"[ceilings] loop mix {mode}: {'; '.join(rate)} at {ghz:.2f} GHz")
+    del src
+    # the 256 x 256 kernel's C drain alone: 64 MiB of 256 x 256 tiles
+    cbufs = [torch.empty((4096, 4096), dtype=torch.int32, device="cuda") for _ in range(8)]
+    k = [0]
+
+    def drain():
+        c = cbufs[k[0] % len(cbufs)]
+        k[0] += 1
+        return lib.tdi8c_store_tiles(c.data_ptr(), 16, 16, 4096, k[0], sh)
+    s = timed(drain, 200)
+    rows.append(("write of 64 MiB as 256 x 256 int32 tiles (4096 x 4096 C, the epilogue's stores alone)",
+                 f"{64 * 2**20 / s / 1e9:.0f} GB/s ({64 * 2**20 / s / 1e9 / HBM_PEAK_GBS:.3f} of 8 TB/s)",
+                 f"{s * 1e6:.2f} µs per launch"))
+    log(f"[ceilings] store tiles 64 MiB: {s * 1e6:.2f} us")
+    del cbufs
     print("| ceiling | rate | note |")
     print("|---|---|---|")
     for r in rows:

@@ -57,6 +57,28 @@ int tdi8c_load16(const int8_t *region, int misalign, int blocks, int iters, int3
 /* A grid of blocks x threads that does nothing. */
 int tdi8c_empty(int blocks, int threads, hipStream_t stream);
 
+/* One K tile of the 256 x 256 GEMM configuration's loop, iters times, in
+ * `blocks` blocks of 512 threads (8 waves): per wave and K step eight
+ * v_mfma_i32_32x32x32_i8 on operands from six ds_read_b128 (the next step's
+ * reads issued before this step's instructions), per K tile 64 KiB moved
+ * into the other half of the 128 KiB LDS by global_load_lds_dwordx4 from a
+ * 64 KiB window of src, then a barrier.  mode: bit 0 the LDS reads, bit 1
+ * the DMA, bit 2 the matrix instructions (a part switched off is left out;
+ * without reads the instructions take register operands).  src: at least
+ * 1 MiB (the LDS starts as a copy of its first 128 KiB, so the operands
+ * are src's bytes); out: 512 int32; cycles: blocks entries.  Per block and
+ * iteration: 256 instructions (16.8 M int8 operations), 192 KiB of LDS
+ * reads, 64 KiB of DMA. */
+int tdi8c_loop_mix(const int8_t *src, int mode, int blocks, int iters, int32_t *out, uint64_t *cycles,
+                   hipStream_t stream);
+
+/* Write tiles_m x tiles_n tiles of 256 x 256 int32 (row stride ldc
+ * elements, at least 256 tiles_n) at C, one block of 512 threads per tile
+ * in the GEMM's XCD-grouped tile order, with non-temporal 16-byte stores of
+ * whole rows (the 256 x 256 kernel's epilogue without its matrix work).
+ * seed: the values written. */
+int tdi8c_store_tiles(int32_t *C, int tiles_m, int tiles_n, int64_t ldc, int seed, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

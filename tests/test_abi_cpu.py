@@ -325,7 +325,8 @@ def test_ceilings_library_exports_its_header():
     header = os.path.join(os.path.dirname(HEADER), "tdi8_ceilings.h")
     text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
     names = sorted(set(re.findall(r"^\s*int\s+(\w+)\s*\(", text, flags=re.M)))
-    assert names == ["tdi8c_dma_read", "tdi8c_empty", "tdi8c_load16", "tdi8c_mfma_loop", "tdi8c_stream_read"]
+    assert names == ["tdi8c_dma_read", "tdi8c_empty", "tdi8c_load16", "tdi8c_loop_mix", "tdi8c_mfma_loop",
+                     "tdi8c_store_tiles", "tdi8c_stream_read"]
     lib = ctypes.CDLL(path)
     for n in names:
         assert hasattr(lib, n), n
@@ -339,6 +340,14 @@ def test_ceilings_library_exports_its_header():
     assert lib.tdi8c_dma_read(None, 1 << 20, 16, 256, 1, C, None) == -1
     assert lib.tdi8c_dma_read(A, 1 << 20, 8, 256, 1, C, None) == -2     # 128 KiB slabs
     assert lib.tdi8c_dma_read(A, 1 << 20, 16, 100, 1, C, None) == -2    # not whole waves
+    lib.tdi8c_loop_mix.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.tdi8c_loop_mix(None, 7, 1, 1, C, C, None) == -1
+    assert lib.tdi8c_loop_mix(A, 8, 1, 1, C, C, None) == -2              # no such mode
+    lib.tdi8c_store_tiles.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_void_p]
+    assert lib.tdi8c_store_tiles(None, 1, 1, 256, 0, None) == -1
+    assert lib.tdi8c_store_tiles(C, 1, 2, 256, 0, None) == -2            # rows shorter than two tiles
 
 
 def test_stamps_library_exports_the_api_and_its_header():
