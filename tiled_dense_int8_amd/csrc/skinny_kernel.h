@@ -208,8 +208,10 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
     static_assert((NROWS * PIECES) % NW == 0, "a chunk's pieces split evenly over the waves");
     // One block row: every B byte is read by one block only, A by all of
     // them; B then streams past the cache (4% at 16 x 8192 x 8192, neutral
-    // at 16 x 4096 x 4096; with two block rows the hint cost 10%).
-    const bool b_once = gridDim.y == 1;
+    // at 16 x 4096 x 4096; with two block rows the hint cost 10%).  Taken
+    // from the arguments, not gridDim: reading the grid size adds the
+    // hidden argument block to the launch (72 -> 328 bytes, ~1% here).
+    const bool b_once = g.tiles_m == 1;
     // The pieces of chunks [c0, c0 + CN) of NROWS rows of one operand (row r
     // at base + r ld, landing in LDS row lds_row0 + r; rows from `valid` on
     // do not exist), enumerated row by row and, within a row, in K order;
@@ -282,26 +284,16 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-    for (int t = tid; t < TILES * 64 * 4; t += WK * 64) (&red[0][0][0])[t] = 0;
-    // The first two chunks go out together (row by row across both), and
-    // are waited for together; chunk c + 2 goes out once chunk c is
-    // consumed, LPW loads per wave.
-    if (nch > 1)
-        issue(0, std::integral_constant<int, 2>{});
-    else if (nch > 0)
-        issue(0, std::integral_constant<int, 1>{});
-#pragma unroll 1
-    for (int c = 0; c < nch; ++c) {
-        if (c > 0 && c + 1 < nch) {
-            TDI8_WAIT_VMCNT(LPW);
-        } else {
-            TDI8_WAIT_VMCNT(0);
-        }
-        block_barrier();
-        const int8_t *b = buf[c & 1];
+    // The S chunks held in the two buffers, wave w taking K positions
+    // [w S KC / WK, (w + 1) S KC / WK) of them (within one chunk: WK is even).
+    auto consume = [&](int c0, auto s_tag) {
+        constexpr int KWS = decltype(s_tag)::value * KC / WK;
+        static_assert(KWS % 64 == 0 && (KC % KWS == 0), "a wave's K range lies in one chunk");
+        const int kw0 = wave * KWS;
+        const int8_t *b = buf[(c0 + kw0 / KC) & 1];
 #pragma unroll
-        for (int kk = 0; kk < KW; kk += 64) {
-            const int k = wave * KW + kk + 16 * grp;
+        for (int kk = 0; kk < KWS; kk += 64) {
+            const int k = kw0 % KC + kk + 16 * grp;
             i32x4 xa[MT], xb[NT];
 #pragma unroll
             for (int i = 0; i < MT; ++i) xa[i] = *reinterpret_cast<const i32x4 *>(b + (16 * i + r16) * RS + k);
@@ -313,17 +305,54 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
                 for (int j = 0; j < NT; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j], xa[i], acc[i][j], 0, 0, 0);
         }
-        if (c + 2 < nch) {
-            TDI8_WAIT_LGKM0();
-            block_barrier();  // every wave is done with this buffer
-            issue(c + 2, std::integral_constant<int, 1>{});
+    };
+    using One = std::integral_constant<int, 1>;
+    using Two = std::integral_constant<int, 2>;
+
+    for (int t = tid; t < TILES * 64 * 4; t += WK * 64) (&red[0][0][0])[t] = 0;
+    if (nch <= 2) {
+        // All of K fits the two buffers: every load goes out at once (row by
+        // row across both chunks), one wait, then the matrix work with each
+        // wave's K range contiguous (16 x 4096 x 4096: 5.35 -> 5.2 us against
+        // the streaming loop below with its wait and barrier per chunk).
+        if (nch == 2)
+            issue(0, Two{});
+        else if (nch == 1)
+            issue(0, One{});
+        TDI8_WAIT_VMCNT(0);
+        __syncthreads();  // also completes the zeroing of red before the atomics
+        if (nch == 2)
+            consume(0, Two{});
+        else if (nch == 1)
+            consume(0, One{});
+    } else {
+        // The first two chunks go out together (row by row across both), and
+        // are waited for together; chunk c + 2 goes out once chunk c is
+        // consumed, LPW loads per wave.
+        issue(0, Two{});
+#pragma unroll 1
+        for (int c = 0; c < nch; ++c) {
+            if (c > 0 && c + 1 < nch) {
+                TDI8_WAIT_VMCNT(LPW);
+            } else {
+                TDI8_WAIT_VMCNT(0);
+            }
+            block_barrier();
+            consume(c, One{});
+            if (c + 2 < nch) {
+                TDI8_WAIT_LGKM0();
+                block_barrier();  // every wave is done with this buffer
+                issue(c + 2, One{});
+            }
         }
     }
     stamp.loop_done();
 
     // Sum the waves' partial tiles: integer addition is exact in any order,
-    // so every wave adds its tile into one LDS copy with atomics.
-    __syncthreads();
+    // so every wave adds its tile into one LDS copy with atomics (the
+    // zeroing of red is complete: the barrier after the single wait above,
+    // or this one after the streaming loop).
+    if (nch > 2) __syncthreads();
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
