@@ -417,7 +417,7 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_rrlds_kernel(GemmArgs g) 
     const int wave = tid >> 6;
     const int r16 = lane & 15;
     const int grp = lane >> 4;
-    const int nb = gridDim.x;
+    const int nb = g.tiles_n;  // the grid's width (from the arguments: reading gridDim adds the hidden argument block)
     const int cb = (nb & 7) == 0 ? (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3) : blockIdx.x;
     const int m0 = blockIdx.y * BM;
     const int n0 = cb * BN;
