@@ -39,8 +39,8 @@
     X(9, 0, 32, 4, 2, 1, 1, 1, 128, 3)  /* 128 x  64, reuse 1 */     \
     X(10, 0, 32, 2, 2, 1, 4, 4, 128, 2) /* 256 x 256, BK 128 */      \
     X(11, 0, 32, 2, 2, 1, 1, 1, 128, 2) /*  64 x  64, reuse 1 */     \
-    X(12, 1, 16, 1, 1, 8, 1, 1, 2048, 2)  /* skinny 16 x 16, 8 K-waves */  \
-    X(13, 1, 16, 1, 1, 16, 1, 1, 2048, 1) /* skinny 16 x 16, 16 K-waves */ \
+    X(12, 1, 16, 1, 1, 16, 1, 1, 2048, 1) /* skinny 16 x 16, 16 K-waves */ \
+    X(13, 1, 16, 1, 1, 8, 1, 1, 2048, 2)  /* skinny 16 x 16, 8 K-waves */  \
     X(14, 1, 16, 1, 1, 4, 1, 1, 2048, 4)  /* skinny 16 x 16, 4 K-waves */  \
     X(15, 1, 16, 1, 1, 8, 1, 2, 1024, 2)  /* skinny 16 x 32, 8 K-waves */  \
     X(16, 1, 16, 1, 1, 8, 2, 1, 1024, 2)  /* skinny 32 x 16, 8 K-waves */  \

@@ -149,13 +149,12 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_kernel(GemmArgs g) {
 // LDS (global_load_lds_dwordx4), so the stream is fully contiguous.  K is
 // taken in chunks of KC bytes, two chunks in flight; a chunk's rows sit in
 // LDS with a 32-byte pad (row stride KC + 32), so the 16 lanes that read
-// one K position of 16 rows hit 16 different bank groups.  With as many A
-// as B rows, half the waves move B and half move A, each operand's rows
-// requested row by row in address order (16 x 4096 x 4096: 5.8 -> 5.4 us
-// against every wave moving pieces of both).  After a chunk lands, wave w
-// consumes K positions w*KC/WK .. (w+1)*KC/WK - 1 of it with
+// one K position of 16 rows hit 16 different bank groups.  After a chunk
+// lands, wave w consumes K positions w*KC/WK .. (w+1)*KC/WK - 1 of it with
 // v_mfma_i32_16x16x64_i8 fed by ds_read_b128, and the WK partial sums are
-// reduced in LDS at the end.
+// reduced in LDS at the end.  When A and B tiles have as many rows and all
+// of K fits the two buffers, a second form below takes the loads with half
+// the waves per operand and a single wait.
 template <int MT, int NT, int WK, int KC>
 __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
     constexpr int BM = 16 * MT;
@@ -189,105 +188,25 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
     const int m0 = blockIdx.y * BM;
     const int n0 = blockIdx.x * BN;
     const int nch = (g.K + KC - 1) / KC;
-    // operand bases and strides as plain values: the load loop then reads
-    // nothing from the argument block (a per-row choice between lda and ldb
-    // otherwise became a vector load whose wait also waited for every DMA
-    // load already issued)
-    const int8_t *const a_base = g.A + static_cast<int64_t>(m0) * g.lda;
-    const int8_t *const b_base = g.B + static_cast<int64_t>(n0) * g.ldb;
-    const int64_t lda = g.lda, ldb = g.ldb;
-    const int kdim = g.K, m_rows = g.M - m0;
-
-    // With as many A rows as B rows, waves [0, WK/2) move B and waves
-    // [WK/2, WK) move A: a wave's loads complete in issue order, so A (an L2
-    // hit for all but the first blocks) never waits behind B's HBM latency
-    // in the same wave.  Otherwise every wave moves pieces of every row.
-    constexpr bool SPLITW = BM == BN && WK % 2 == 0;
-    constexpr int NW = SPLITW ? WK / 2 : WK;          // waves sharing a row range
-    constexpr int NROWS = SPLITW ? BM : ROWS;         // rows of that range
-    static_assert((NROWS * PIECES) % NW == 0, "a chunk's pieces split evenly over the waves");
     // One block row: every B byte is read by one block only, A by all of
     // them; B then streams past the cache (4% at 16 x 8192 x 8192, neutral
     // at 16 x 4096 x 4096; with two block rows the hint cost 10%).  Taken
     // from the arguments, not gridDim: reading the grid size adds the
     // hidden argument block to the launch (72 -> 328 bytes, ~1% here).
     const bool b_once = g.tiles_m == 1;
-    // The pieces of chunks [c0, c0 + CN) of NROWS rows of one operand (row r
-    // at base + r ld, landing in LDS row lds_row0 + r; rows from `valid` on
-    // do not exist), enumerated row by row and, within a row, in K order;
-    // piece x goes to the range's wave x % NW, so its NW waves request
-    // consecutive kilobytes of a row together and a row's requests reach
-    // memory in address order.  Rows that do not exist (A rows past a ragged
-    // M, e.g. M < 16) and the 16-byte pieces at or past K of a last, partial
-    // chunk (K a multiple of 16) read the zero chunk.  NTF: the stream hint.
-    // Each operand has a loop of its own with the hint fixed (one loop for
-    // both operands, choosing base, stride and hint per wave at run time,
-    // was 6% slower in a standalone copy of this kernel).
-    auto issue_rows = [&](const int8_t *base, int64_t ld, int valid, int lds_row0, int rw, int c0, auto cn_tag,
-                          auto nt_tag) {
-        constexpr int CN = decltype(cn_tag)::value;
-        constexpr int PR = CN * PIECES;   // pieces per row
-        constexpr int NTF = decltype(nt_tag)::value;
-        const int8_t *const cbase = base + c0 * KC + 16 * lane;
-        if ((c0 + CN) * KC <= kdim && valid >= NROWS) {
-            // every piece exists
-            for (int x = rw; x < NROWS * PR; x += NW) {
-                const int r = x / PR, pc = x % PR;
-                __builtin_amdgcn_global_load_lds(cbase + r * ld + pc * 1024,
-                                                 (lds_void_t *)(buf[(c0 + pc / PIECES) & 1] + (lds_row0 + r) * RS +
-                                                                (pc % PIECES) * 1024),
-                                                 16, 0, NTF);
-            }
-        } else {
-            for (int x = rw; x < NROWS * PR; x += NW) {
-                const int r = x / PR, pc = x % PR;
-                const bool ok = c0 * KC + pc * 1024 + 16 * lane < kdim && r < valid;
-                __builtin_amdgcn_global_load_lds(ok ? cbase + r * ld + pc * 1024 : zero_chunk,
-                                                 (lds_void_t *)(buf[(c0 + pc / PIECES) & 1] + (lds_row0 + r) * RS + (pc % PIECES) * 1024),
-                                                 16, 0, NTF);
-            }
-        }
-    };
-    using NoHint = std::integral_constant<int, 0>;
-    using StreamHint = std::integral_constant<int, kLoadStream>;
-    auto issue = [&](int c0, auto cn_tag) {
-        if constexpr (SPLITW) {
-            if (wave < WK / 2) {
-                if (b_once)
-                    issue_rows(b_base, ldb, BN, BM, wave, c0, cn_tag, StreamHint{});
-                else
-                    issue_rows(b_base, ldb, BN, BM, wave, c0, cn_tag, NoHint{});
-            } else {
-                issue_rows(a_base, lda, m_rows, 0, wave - WK / 2, c0, cn_tag, NoHint{});
-            }
-        } else {
-            // rows [0, BM) of A then [BM, ROWS) of B, every wave both
-            constexpr int PR = decltype(cn_tag)::value * PIECES;
-            for (int x = wave; x < NROWS * PR; x += NW) {
-                const int row = x / PR, pc = x % PR;
-                const int k = c0 * KC + pc * 1024 + 16 * lane;
-                const bool is_a = row < BM;
-                const bool ok = k < kdim && (!is_a || row < m_rows);
-                const int8_t *src = !ok ? zero_chunk : is_a ? a_base + row * lda + k : b_base + (row - BM) * ldb + k;
-                lds_void_t *dst = (lds_void_t *)(buf[(c0 + pc / PIECES) & 1] + row * RS + (pc % PIECES) * 1024);
-                if (b_once && !is_a)
-                    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kLoadStream);
-                else
-                    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-            }
-        }
-    };
 
     i32x4 acc[MT][NT];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+    for (int t = tid; t < TILES * 64 * 4; t += WK * 64) (&red[0][0][0])[t] = 0;
 
-    // The S chunks held in the two buffers, wave w taking K positions
-    // [w S KC / WK, (w + 1) S KC / WK) of them (within one chunk: WK is even).
-    auto consume = [&](int c0, auto s_tag) {
-        constexpr int KWS = decltype(s_tag)::value * KC / WK;
+    // Matrix work on the S chunks held in the two buffers from chunk c0 by
+    // W waves, wave w taking K positions [w S KC / W, (w + 1) S KC / W) of
+    // them (within one chunk: W is even).
+    auto consume = [&](int c0, auto s_tag, auto w_tag) {
+        constexpr int KWS = decltype(s_tag)::value * KC / decltype(w_tag)::value;
         static_assert(KWS % 64 == 0 && (KC % KWS == 0), "a wave's K range lies in one chunk");
         const int kw0 = wave * KWS;
         const int8_t *b = buf[(c0 + kw0 / KC) & 1];
@@ -309,50 +228,126 @@ __global__ void __launch_bounds__(WK * 64) gemm_skinny_lds_kernel(GemmArgs g) {
     using One = std::integral_constant<int, 1>;
     using Two = std::integral_constant<int, 2>;
 
-    for (int t = tid; t < TILES * 64 * 4; t += WK * 64) (&red[0][0][0])[t] = 0;
-    if (nch <= 2) {
-        // All of K fits the two buffers: every load goes out at once (row by
-        // row across both chunks), one wait, then the matrix work with each
-        // wave's K range contiguous (16 x 4096 x 4096: 5.35 -> 5.2 us against
-        // the streaming loop below with its wait and barrier per chunk).
-        if (nch == 2)
-            issue(0, Two{});
-        else if (nch == 1)
-            issue(0, One{});
+    // As many A rows as B rows and all of K within the two buffers (the
+    // M = 16 headline, K <= 2 KC): waves [0, WK/2) move B and waves [WK/2,
+    // WK) move A, so A (an L2 hit for all but the first blocks) never
+    // waits behind B's HBM latency in the same wave (a wave's loads
+    // complete in issue order); each operand's rows are requested row by
+    // row, the pieces of a row in K order across both chunks (its requests
+    // reach memory in address order); one wait, then the matrix work.
+    // 16 x 4096 x 4096, column-major B: 5.7 -> 5.25 us against the general
+    // loop below, measured side by side on one device.  Elsewhere the
+    // general loop stays faster (longer K: 32 x 4096 x 8192 took 16.4 us
+    // in this form against 11.8).
+    constexpr bool SPLITW = BM == BN && WK % 2 == 0;
+    // at most 8 waves take part (4 per operand: 16 x 4096 x 4096 ran 5.25 us
+    // with 8 and 5.5 with 16); the others only keep the block's barriers
+    constexpr int FW = WK < 8 ? WK : 8;
+    if (SPLITW && nch <= 2) {
+        constexpr int NW = FW / 2;                       // waves per operand
+        constexpr int PR = 2 * PIECES;                   // pieces per row over both chunks
+        const bool b_wave = wave < NW;
+        const int rw = b_wave ? wave : wave - NW;
+        const int8_t *base = b_wave ? g.B + static_cast<int64_t>(n0) * g.ldb : g.A + static_cast<int64_t>(m0) * g.lda;
+        const int64_t ld = b_wave ? g.ldb : g.lda;
+        const int valid = b_wave ? BN : g.M - m0;        // A rows past M read the zero chunk
+        const int row0 = b_wave ? BM : 0;
+        const int kdim = g.K;
+        // rows of this wave's operand, pieces x = rw, rw + NW, ... of the
+        // row-major enumeration; the 16-byte pieces at or past K of a last,
+        // partial chunk (K a multiple of 16) read the zero chunk
+        auto issue_rows = [&](auto nt_tag) {
+            constexpr int NTF = decltype(nt_tag)::value;
+            for (int x = rw; x < BM * PR; x += NW) {
+                const int r = x / PR, pc = x % PR;
+                const int k = pc * 1024 + 16 * lane;
+                const int8_t *src = k < kdim && r < valid ? base + r * ld + k : zero_chunk;
+                __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(buf[pc / PIECES] + (row0 + r) * RS + (pc % PIECES) * 1024),
+                                                 16, 0, NTF);
+            }
+        };
+        if (wave < FW) {
+            if (!b_wave)
+                issue_rows(std::integral_constant<int, 0>{});
+            else if (b_once)
+                issue_rows(std::integral_constant<int, kLoadStream>{});
+            else
+                issue_rows(std::integral_constant<int, 0>{});
+        }
         TDI8_WAIT_VMCNT(0);
-        __syncthreads();  // also completes the zeroing of red before the atomics
-        if (nch == 2)
-            consume(0, Two{});
-        else if (nch == 1)
-            consume(0, One{});
+        __syncthreads();
+        if (wave < FW) {
+            if (nch == 2)
+                consume(0, Two{}, std::integral_constant<int, FW>{});
+            else if (nch == 1)
+                consume(0, One{}, std::integral_constant<int, FW>{});
+        }
     } else {
-        // The first two chunks go out together (row by row across both), and
-        // are waited for together; chunk c + 2 goes out once chunk c is
-        // consumed, LPW loads per wave.
-        issue(0, Two{});
-#pragma unroll 1
+        // A rows past M (a ragged M, e.g. M < 16) read the zero chunk (ok
+        // false), and so do the 16-byte pieces at or past K of a last,
+        // partial chunk (K a multiple of 16; kin: the piece's K offset
+        // within a chunk).  Two chunks in flight.
+        const int8_t *src[LPW];
+        int dst_off[LPW], kin[LPW];
+        bool ok[LPW];
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int x = i * WK + wave;
+            const int row = x / PIECES;
+            const int piece = x % PIECES;
+            kin[i] = piece * 1024 + 16 * lane;
+            ok[i] = row >= BM || m0 + row < g.M;
+            src[i] = (row < BM ? g.A + static_cast<int64_t>(ok[i] ? m0 + row : m0) * g.lda
+                               : g.B + static_cast<int64_t>(n0 + row - BM) * g.ldb) + piece * 1024 + 16 * lane;
+            dst_off[i] = row * RS + piece * 1024;
+        }
+        auto issue = [&](int c) {
+#pragma unroll
+            for (int i = 0; i < LPW; ++i) {
+                const int8_t *p = ok[i] && c * KC + kin[i] < g.K ? src[i] + c * KC : zero_chunk;
+                if (b_once && (i * WK + wave) / PIECES >= BM)
+                    __builtin_amdgcn_global_load_lds(p, (lds_void_t *)(buf[c & 1] + dst_off[i]), 16, 0, kLoadStream);
+                else
+                    __builtin_amdgcn_global_load_lds(p, (lds_void_t *)(buf[c & 1] + dst_off[i]), 16, 0, 0);
+            }
+        };
+        if (nch > 0) issue(0);
+        if (nch > 1) issue(1);
         for (int c = 0; c < nch; ++c) {
-            if (c > 0 && c + 1 < nch) {
+            if (c + 1 < nch) {
                 TDI8_WAIT_VMCNT(LPW);
             } else {
                 TDI8_WAIT_VMCNT(0);
             }
             block_barrier();
-            consume(c, One{});
+            const int8_t *b = buf[c & 1];
+#pragma unroll
+            for (int kk = 0; kk < KW; kk += 64) {
+                const int k = wave * KW + kk + 16 * grp;
+                i32x4 xa[MT], xb[NT];
+#pragma unroll
+                for (int i = 0; i < MT; ++i) xa[i] = *reinterpret_cast<const i32x4 *>(b + (16 * i + r16) * RS + k);
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    xb[j] = *reinterpret_cast<const i32x4 *>(b + (BM + 16 * j + r16) * RS + k);
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j], xa[i], acc[i][j], 0, 0, 0);
+            }
             if (c + 2 < nch) {
                 TDI8_WAIT_LGKM0();
                 block_barrier();  // every wave is done with this buffer
-                issue(c + 2, One{});
+                issue(c + 2);
             }
         }
     }
     stamp.loop_done();
 
     // Sum the waves' partial tiles: integer addition is exact in any order,
-    // so every wave adds its tile into one LDS copy with atomics (the
-    // zeroing of red is complete: the barrier after the single wait above,
-    // or this one after the streaming loop).
-    if (nch > 2) __syncthreads();
+    // so every wave adds its tile into one LDS copy with atomics.
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
