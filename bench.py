@@ -442,6 +442,74 @@ SWEEPS = {
 }
 
 
+PERSIST_SHAPES = [(4096, 4096, 4096), (8192, 8192, 4096), (8192, 8192, 8192), (16384, 16384, 8192)]
+
+
+def persistent_report(t, shapes=None):
+    """The persistent whole-tile form (gemm_s8s8s32_persistent, one wave of
+    resident blocks walking the tiles, C stored from registers while the next
+    tile computes) against the default call (one block per tile) on the
+    selected configuration, both B layouts, inputs rotating as in the
+    headline timing.  The two C must be equal byte for byte.  Rounds of
+    launches alternate between the two forms; medians of 5 rounds, HIP
+    events.  Prints a markdown table."""
+    import torch
+    torch.manual_seed(0)
+    sh = torch.cuda.current_stream().cuda_stream
+    props = torch.cuda.get_device_properties(0)
+    print("| M×N×K | B | configuration | tiles | default µs (one block per tile) | persistent µs (blocks) | "
+          "persistent / default |")
+    print("|---|---|---|---|---|---|---|")
+    for (M, N, K) in shapes or PERSIST_SHAPES:
+        cfg = t.tile_config_info(t.select_tile_config(M, N, K))
+        tiles = (M // cfg.block_m) * (N // cfg.block_n)
+        nb = props.multi_processor_count * max(cfg.blocks_per_cu, 1)
+        nb = min(nb - nb % 8 if nb >= 8 else nb, tiles)
+        for bcm in (True, False):
+            w = dict(M=M, N=N, K=K, bcm=bcm)
+            nsets = rotation_sets(w)
+            sets = [(torch.randint(-128, 128, (M, K), dtype=torch.int8, device="cuda"),
+                     torch.randint(-128, 128, (N, K) if bcm else (K, N), dtype=torch.int8, device="cuda"),
+                     torch.empty((M, N), dtype=torch.int32, device="cuda")) for _ in range(nsets)]
+            fn = t.gemm_s8s8s32_bt if bcm else t.gemm_s8s8s32
+
+            def default(i):
+                a, b, c = sets[i % nsets]
+                return fn(M, N, K, a.data_ptr(), K, b.data_ptr(), b.stride(0), c.data_ptr(), N, sh)
+
+            def persistent(i):
+                a, b, c = sets[i % nsets]
+                return t.gemm_s8s8s32_persistent(cfg.id, bcm, M, N, K, a.data_ptr(), K, b.data_ptr(), b.stride(0),
+                                                 c.data_ptr(), N, 0, sh)
+            assert default(0) == t.OK
+            ref = sets[0][2].clone()
+            sets[0][2].fill_(-1)
+            assert persistent(0) == t.OK
+            torch.cuda.synchronize()
+            assert torch.equal(ref, sets[0][2]), ("persistent form differs", M, N, K, bcm)
+            del ref
+            reps = int(max(5, min(2000, 0.15 / (2.0 * M * N * K / 2.0e15))))
+            for i in range(2 * reps):
+                (default if i % 2 else persistent)(i)
+            torch.cuda.synchronize()
+            res = {"default": [], "persistent": []}
+            for r in range(5):
+                for name in (["default", "persistent"] if r % 2 == 0 else ["persistent", "default"]):
+                    f = default if name == "default" else persistent
+                    e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for i in range(reps):
+                        f(i)
+                    e1.record(); e1.synchronize()
+                    res[name].append(e0.elapsed_time(e1) * 1e3 / reps)
+            d = sorted(res["default"])[2]
+            p = sorted(res["persistent"])[2]
+            print(f"| {M}×{N}×{K} | {'col' if bcm else 'row'} | {cfg.id} | {tiles} | {d:.1f} | {p:.1f} ({nb}) | "
+                  f"{p / d:.3f} |", flush=True)
+            del sets
+            torch.cuda.empty_cache()
+
+
 def fit_line(xs, ys):
     """Least-squares slope and intercept of ys against xs."""
     n = len(xs)
@@ -845,6 +913,9 @@ def main():
     ap.add_argument("--stamps", action="store_true",
                     help="only print per-block timelines (clock, K loop vs epilogue) of every workload's kernel "
                          "from the instrumented build libtdi8_stamps.so")
+    ap.add_argument("--persistent-report", default=None, nargs="?", const="all", metavar="MxNxK",
+                    help="only time the persistent whole-tile form against the default call (all shapes of the "
+                         "suite, or the one given)")
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="only summarise a rocprofv3 kernel trace of a --sweep run (needs --plan)")
     args = ap.parse_args()
@@ -879,6 +950,11 @@ def main():
         return
     if args.sweep:
         k_sweep(t, args.sweep, args.plan)
+        return
+    if args.persistent_report:
+        shapes = None if args.persistent_report == "all" else [
+            tuple(int(x) for x in args.persistent_report.split("x"))]
+        persistent_report(t, shapes)
         return
     if args.stamps:
         first = args.workload if args.workload in WORKLOADS else "square4096"

@@ -228,8 +228,10 @@ typedef enum {
     TDI8_FORM_SKINNY_DMA = 6,       /* skinny kernel fed by LDS DMA (either B layout) */
     TDI8_FORM_SKINNY_PREDICATED = 7,/* skinny kernel with masked register loads */
     TDI8_FORM_SKINNY_ROW_GROUPS = 8,/* zero fill, then the row-major-B column groups of a skinny tile */
-    TDI8_FORM_PREDICATED_PREFETCH = 9 /* the predicated kernel with two K tiles of loads in flight:
+    TDI8_FORM_PREDICATED_PREFETCH = 9, /* the predicated kernel with two K tiles of loads in flight:
                                        * column-major B, at most one block per compute unit */
+    TDI8_FORM_PERSISTENT = 10       /* persistent whole-tile kernel: a fixed grid walks the tiles
+                                       (gemm_s8s8s32_persistent) */
 } tdi8_form;
 
 typedef struct {
@@ -255,6 +257,29 @@ typedef struct {
  * query, so the plan is what runs.  Host only; initialises the device. */
 int gemm_plan(int config_id, int b_col_major, int M, int N, int K, const int8_t *A, int lda, const int8_t *B,
               int ldb, const int32_t *C, int ldc, tdi8_plan *out);
+
+/* Same product in the persistent form of a general configuration's
+ * whole-tile kernel: `blocks` blocks (0: as many as the device holds at once,
+ * the compute units times the configuration's resident blocks per unit,
+ * rounded down to a multiple of 8; any value is capped at the tile count)
+ * each walk the tiles blocks apart in the block-to-tile order of the other
+ * forms, which groups the tiles resident on one XCD into a compact region
+ * (the contest write-up "先导杯比赛回顾", Swizzle 线程块映射: block order
+ * chosen for cache reuse; 矩阵维度高度不均衡: flat waves of blocks lose it).
+ * A block's K tiles form one load stream across its tiles, and each finished
+ * tile is stored from the accumulation registers while the next tile's
+ * matrix work runs, so the C write of one tile overlaps the next one's
+ * product.  config_id -1 takes the selection's configuration.  Needs whole
+ * tiles of that configuration (M, N, K multiples of its block_m, block_n,
+ * block_k), A, B and C 16-byte aligned, lda and ldb multiples of 16 and ldc
+ * a multiple of 4; otherwise, or for a skinny configuration, returns
+ * TDI8_ERR_BAD_CONFIG and enqueues nothing.  blocks < 0 gives
+ * TDI8_ERR_INVALID_VALUE; M == 0 or N == 0 enqueues nothing and returns
+ * TDI8_OK.  Arguments, layouts, ownership and the other errors as for
+ * gemm_s8s8s32_with_config.  The result is bit-identical to
+ * the other forms' (integer sums). */
+int gemm_s8s8s32_persistent(int config_id, int b_col_major, int M, int N, int K, const int8_t *A, int lda,
+                            const int8_t *B, int ldb, int32_t *C, int ldc, int blocks, hipStream_t stream);
 
 /* ---- int8 2-D convolution (implicit GEMM on the same kernels) ----------------
  *

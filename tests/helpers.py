@@ -49,8 +49,12 @@ class DeviceCase:
         self.C_ptr = self.c_buf.data_ptr() + 4 * oc
         self.oc = oc
 
-    def run(self, entry, config=None, stream=0):
+    def run(self, entry, config=None, stream=0, persistent=None):
         import tiled_dense_int8_amd as t
+        if persistent is not None:
+            return t.gemm_s8s8s32_persistent(-1 if config is None else config, self.bcm, self.M, self.N, self.K,
+                                             self.A_ptr, self.lda, self.B_ptr, self.ldb, self.C_ptr, self.ldc,
+                                             persistent, stream)
         args = (self.M, self.N, self.K, self.A_ptr, self.lda, self.B_ptr, self.ldb, self.C_ptr, self.ldc, stream)
         if config is not None:
             return t.gemm_s8s8s32_with_config(config, self.bcm, *args)
@@ -72,11 +76,11 @@ class DeviceCase:
         return oracle.gemm(self.A_store, self.B_store, self.bcm, M=self.M, N=self.N, K=self.K)
 
 
-def check_case(case: DeviceCase, entry_desc: str, config=None, expect=None):
+def check_case(case: DeviceCase, entry_desc: str, config=None, expect=None, persistent=None):
     import tiled_dense_int8_amd as t
     note(f"[case] {entry_desc} M={case.M} N={case.N} K={case.K} bcm={case.bcm} lda={case.lda} "
-         f"ldb={case.ldb} ldc={case.ldc} config={config}")
-    st = case.run(None, config=config)
+         f"ldb={case.ldb} ldc={case.ldc} config={config} persistent={persistent}")
+    st = case.run(None, config=config, persistent=persistent)
     assert st == t.OK, t.tdi8_status_string(st)
     C, rest = case.result()
     want = expect if expect is not None else case.oracle()

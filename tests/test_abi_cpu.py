@@ -79,6 +79,15 @@ def test_entry_points_reject_before_any_device_work():
     assert t.gemm_s8s8s32_with_config(-1, 1, 4, 4, 4, A, 4, B, 4, C, 4, 0) == t.ERR_BAD_CONFIG
     assert t.gemm_s8s8s32(0, 4, 4, 0, 4, 0, 4, 0, 4, 0) == t.OK
     assert t.select_tile_config(-1, 1, 1) == t.ERR_INVALID_VALUE
+    # the persistent form: same argument checks, then its own
+    p = t.gemm_s8s8s32_persistent
+    assert p(0, 1, -1, 4, 4, A, 4, B, 4, C, 4, 0, 0) == t.ERR_INVALID_VALUE
+    assert p(0, 1, 4, 4, 4, None, 4, B, 4, C, 4, 0, 0) == t.ERR_NULL_POINTER
+    assert p(0, 0, 4, 4, 4, A, 4, B, 4, A + 2, 4, 0, 0) == t.ERR_ALIASING
+    assert p(99, 1, 4, 4, 4, A, 4, B, 4, C, 4, 0, 0) == t.ERR_BAD_CONFIG
+    assert p(-2, 1, 4, 4, 4, A, 4, B, 4, C, 4, 0, 0) == t.ERR_BAD_CONFIG
+    assert p(0, 1, 4, 4, 4, A, 4, B, 4, C, 4, -1, 0) == t.ERR_INVALID_VALUE
+    assert p(0, 1, 0, 4, 4, 0, 4, 0, 4, 0, 4, 0, 0) == t.OK
 
 
 def library_table():

@@ -1,0 +1,98 @@
+"""Persistent whole-tile form (gemm_s8s8s32_persistent) against the CPU
+oracle, through the C ABI: every general configuration, both B layouts,
+block counts that give every block one tile, several tiles, or unequal
+numbers of tiles, K tile streams shorter and longer than the pipeline,
+K = 0, and the 4096^3 workload in full.  Bit-exact on every element; C
+sits in a sentinel-filled buffer that must survive outside the window."""
+import numpy as np
+import pytest
+
+import synthetic
+from helpers import DeviceCase, check_case, note
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiled_dense_int8_amd as t
+    return t
+
+
+def general(t):
+    return [c for c in (t.tile_config_info(i) for i in range(t.tile_config_count())) if c.family == 0]
+
+
+def cases_for(c):
+    BM, BN, BK = c.block_m, c.block_n, c.block_k
+    return [
+        ((BM, BN, BK), 0),            # one tile, one K tile (shorter than the pipeline)
+        ((2 * BM, 3 * BN, 5 * BK), 0),  # one tile per block, five K tiles
+        ((2 * BM, 3 * BN, 5 * BK), 4),  # six tiles on four blocks: two blocks take two
+        ((3 * BM, BN, 2 * BK), 1),    # one block walks three tiles of two K tiles
+        ((2 * BM, 2 * BN, BK), 3),    # one K tile per tile: the stream crosses a tile every step
+        ((BM, 4 * BN, 3 * BK), 2),    # two tiles per block along N
+    ]
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_persistent_every_general_config(lib, bcm):
+    t = lib
+    for c in general(t):
+        for (M, N, K), blocks in cases_for(c):
+            A, B = synthetic.gemm_inputs(M, N, K, seed=M + 3 * N + 11 * K + blocks)
+            case = DeviceCase(A, B, bcm)
+            check_case(case, f"persistent[{c.id}] blocks={blocks}", config=c.id, persistent=blocks)
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_persistent_k_zero_and_padded(lib, bcm):
+    """K = 0 stores zero tiles; padded leading dimensions (multiples of 16)
+    keep the pads untouched."""
+    t = lib
+    c = t.tile_config_info(0)
+    M, N = 2 * c.block_m, c.block_n
+    A, B = synthetic.gemm_inputs(M, N, 0, seed=5)
+    case = DeviceCase(A, B, bcm, lda=16, ldb=16 if bcm else N)
+    check_case(case, "persistent K=0", config=0, persistent=1, expect=np.zeros((M, N), np.int32))
+    M, N, K = c.block_m, 2 * c.block_n, 3 * c.block_k
+    A, B = synthetic.gemm_inputs(M, N, K, seed=6)
+    case = DeviceCase(A, B, bcm, lda=K + 32, ldb=(K + 48) if bcm else (N + 16), ldc=N + 4)
+    check_case(case, "persistent padded", config=0, persistent=1)
+
+
+def test_persistent_rejects_what_it_cannot_run(lib):
+    t = lib
+    c = t.tile_config_info(0)
+    M, N, K = c.block_m, c.block_n, c.block_k
+    A, B = synthetic.gemm_inputs(M + 1, N, K, seed=1)
+    ragged = DeviceCase(A, B, True)
+    assert ragged.run(None, config=0, persistent=0) == t.ERR_BAD_CONFIG
+    A, B = synthetic.gemm_inputs(M, N, K, seed=2)
+    case = DeviceCase(A, B, True, lda=K + 1)
+    assert case.run(None, config=0, persistent=0) == t.ERR_BAD_CONFIG
+    skinny = [x.id for x in (t.tile_config_info(i) for i in range(t.tile_config_count())) if x.family == 1]
+    case = DeviceCase(A, B, True)
+    assert case.run(None, config=skinny[0], persistent=0) == t.ERR_BAD_CONFIG
+    assert case.run(None, config=0, persistent=-1) == t.ERR_INVALID_VALUE
+    # nothing was written
+    C, rest = case.result()
+    assert (C == -123456789).all() and (rest == -123456789).all()
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_persistent_workload_4096(lib, bcm):
+    """4096^3 in full against the oracle: one tile per block (the default
+    grid of 256 blocks) and two tiles per block (128 blocks)."""
+    M = N = K = 4096
+    A, B = synthetic.gemm_inputs(M, N, K, 0)
+    case = DeviceCase(A, B, bcm)
+    want = case.oracle()
+    for blocks in (0, 128):
+        note(f"[case] persistent 4096^3 bcm={bcm} blocks={blocks}")
+        case.c_buf.fill_(-123456789)
+        check_case(case, f"persistent 4096^3 blocks={blocks}", persistent=blocks, expect=want)

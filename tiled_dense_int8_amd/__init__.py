@@ -54,7 +54,8 @@ class Selection(ctypes.Structure):
 
 
 FORM_NONE, FORM_PREDICATED, FORM_PIPELINED, FORM_PIPELINED_EDGE, FORM_SPLIT, FORM_SPLIT_EDGE, \
-    FORM_SKINNY_DMA, FORM_SKINNY_PREDICATED, FORM_SKINNY_ROW_GROUPS, FORM_PREDICATED_PREFETCH = range(10)
+    FORM_SKINNY_DMA, FORM_SKINNY_PREDICATED, FORM_SKINNY_ROW_GROUPS, FORM_PREDICATED_PREFETCH, \
+    FORM_PERSISTENT = range(11)
 
 
 class Plan(ctypes.Structure):
@@ -71,6 +72,7 @@ _SIGNATURES = {
     "gemm_s8s8s32": (_i, _GEMM_ARGS),
     "gemm_s8s8s32_bt": (_i, _GEMM_ARGS),
     "gemm_s8s8s32_with_config": (_i, [_i, _i] + _GEMM_ARGS),
+    "gemm_s8s8s32_persistent": (_i, [_i, _i] + _GEMM_ARGS[:-1] + [_i, _GEMM_ARGS[-1]]),
     "select_tile_config": (_i, [_i, _i, _i]),
     "tile_config_count": (_i, []),
     "tile_config_info": (_i, [_i, ctypes.POINTER(TileConfig)]),
@@ -144,6 +146,12 @@ def gemm_s8s8s32_with_config(config_id, b_col_major, M, N, K, A, lda, B, ldb, C,
     _int32(config_id=config_id, M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     return _lib.gemm_s8s8s32_with_config(config_id, 1 if b_col_major else 0, M, N, K, A, lda, B, ldb,
                                          C, ldc, stream)
+
+
+def gemm_s8s8s32_persistent(config_id, b_col_major, M, N, K, A, lda, B, ldb, C, ldc, blocks=0, stream=0) -> int:
+    _int32(config_id=config_id, M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc, blocks=blocks)
+    return _lib.gemm_s8s8s32_persistent(config_id, 1 if b_col_major else 0, M, N, K, A, lda, B, ldb,
+                                        C, ldc, blocks, stream)
 
 
 def gemm_plan(config_id, b_col_major, M, N, K, A, lda, B, ldb, C, ldc) -> Plan:
@@ -227,7 +235,7 @@ def _device_of(*tensors) -> "torch.device":
 
 
 def gemm(A: "torch.Tensor", B: "torch.Tensor", b_col_major: bool, out: "torch.Tensor | None" = None,
-         config: int | None = None, stream=None) -> "torch.Tensor":
+         config: int | None = None, stream=None, persistent_blocks: int | None = None) -> "torch.Tensor":
     """C = A x B on the GPU.
 
     A: int8 (M, K) with unit column stride (row stride = lda).
@@ -235,6 +243,8 @@ def gemm(A: "torch.Tensor", B: "torch.Tensor", b_col_major: bool, out: "torch.Te
        b_col_major is False, (N, K) with K contiguous if True.
     out: optional int32 (M, N) with unit column stride (row stride = ldc).
     config: run this configuration id instead of the selected one.
+    persistent_blocks: run the persistent whole-tile form with this many
+       blocks (0: one wave of resident blocks); needs whole tiles.
     """
     if A.dtype != torch.int8 or B.dtype != torch.int8:
         raise TypeError("A and B must be int8")
@@ -253,7 +263,10 @@ def gemm(A: "torch.Tensor", B: "torch.Tensor", b_col_major: bool, out: "torch.Te
     _int32(M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     with torch.cuda.device(dev):
         s = _stream_handle(stream)
-        if config is None:
+        if persistent_blocks is not None:
+            st = gemm_s8s8s32_persistent(-1 if config is None else config, b_col_major, M, N, K, A.data_ptr(),
+                                         lda, B.data_ptr(), ldb, out.data_ptr(), ldc, persistent_blocks, s)
+        elif config is None:
             fn = gemm_s8s8s32_bt if b_col_major else gemm_s8s8s32
             st = fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, s)
         else:

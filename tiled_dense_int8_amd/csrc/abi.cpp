@@ -144,6 +144,7 @@ struct Plan {
     bool zero_first = false;  // a fill kernel zeroes the C window first (K split)
     dim3 grid, block;
     GemmArgs g{};
+    int nblocks = 0;          // persistent form: its block count, the kernel's second argument
 };
 
 int make_plan(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
@@ -251,6 +252,7 @@ int make_plan(int id, int bcol, int M, int N, int K, const int8_t *A, int lda, c
 int run_plan(Plan &p, hipStream_t stream) {
     attach_stamps(p.g);
     void *args[] = {&p.g};
+    void *pargs[] = {&p.g, &p.nblocks};  // the persistent kernel's two arguments
     hipError_t e;
     if (p.zero_first) {
         const int64_t quads = static_cast<int64_t>(p.g.M) * ((p.g.N + 3) / 4);
@@ -258,7 +260,7 @@ int run_plan(Plan &p, hipStream_t stream) {
         e = hipLaunchKernel(reinterpret_cast<const void *>(&zero_c_kernel), dim3(zb), dim3(256), args, 0, stream);
         if (e != hipSuccess) return hip_fail(e);
     }
-    e = hipLaunchKernel(p.kernel, p.grid, p.block, args, 0, stream);
+    e = hipLaunchKernel(p.kernel, p.grid, p.block, p.form == TDI8_FORM_PERSISTENT ? pargs : args, 0, stream);
     if (e != hipSuccess) return hip_fail(e);
     return TDI8_OK;
 }
@@ -304,6 +306,55 @@ int gemm_entry(int cfg, int bcol, int M, int N, int K, const int8_t *A, int lda,
     int id = -1;
     st = plan_call(cfg, bcol, M, N, K, A, lda, B, ldb, C, ldc, *ds, &p, &id);
     if (st != TDI8_OK) return st;
+    return run_plan(p, stream);
+}
+
+// The persistent form of configuration id (general family) over whole tiles;
+// blocks 0 = one wave of resident blocks, rounded down to a multiple of 8.
+int persistent_entry(int cfg, int bcol, int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
+                     int32_t *C, int ldc, int blocks, hipStream_t stream) {
+    int st = tdi8_validate(bcol, M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != TDI8_OK) return st;
+    if (cfg >= TDI8_NUM_CONFIGS || cfg < -1) return TDI8_ERR_BAD_CONFIG;
+    if (blocks < 0) return TDI8_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) return TDI8_OK;
+    DeviceState *ds = current_device(&st);
+    if (!ds) return st;
+    const int id = cfg < 0 ? select_config(M, N, K, ds->hw, ds->bpc, nullptr) : cfg;
+    if (id < 0) return id;
+    const StaticCfg c = static_cfg(id);
+    if (c.family != 0) return TDI8_ERR_BAD_CONFIG;
+    const bool whole = M % c.bm == 0 && N % c.bn == 0 && K % c.bk == 0;
+    const bool al = aligned(A, 16) && lda % 16 == 0 && aligned(B, 16) && ldb % 16 == 0 && aligned(C, 16) &&
+                    ldc % 4 == 0;
+    if (!whole || !al) return TDI8_ERR_BAD_CONFIG;
+    const int64_t tiles = static_cast<int64_t>(M / c.bm) * (N / c.bn);
+    if (tiles > INT_MAX / c.threads) return TDI8_ERR_INVALID_VALUE;
+    int64_t nb = blocks;
+    if (nb == 0) {
+        nb = static_cast<int64_t>(ds->hw.num_cu) * (ds->bpc[id] > 0 ? ds->bpc[id] : 1);
+        if (nb >= 8) nb -= nb % 8;
+    }
+    if (nb > tiles) nb = tiles;
+    Plan p;
+    p.form = TDI8_FORM_PERSISTENT;
+    p.kernel = kernels()[id].persist[bcol ? 1 : 0];
+    p.block = dim3(c.threads);
+    p.grid = dim3(static_cast<unsigned>(nb));
+    p.nblocks = static_cast<int>(nb);
+    GemmArgs &g = p.g;
+    g.A = A;
+    g.B = B;
+    g.C = C;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.ldc = ldc;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.tiles_m = M / c.bm;
+    g.tiles_n = N / c.bn;
+    g.splits = 1;
     return run_plan(p, stream);
 }
 
@@ -444,6 +495,11 @@ int gemm_s8s8s32_with_config(int config_id, int b_col_major, int M, int N, int K
                              const int8_t *B, int ldb, int32_t *C, int ldc, hipStream_t stream) {
     if (config_id < 0 || config_id >= TDI8_NUM_CONFIGS) return TDI8_ERR_BAD_CONFIG;
     return gemm_entry(config_id, b_col_major ? 1 : 0, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_s8s8s32_persistent(int config_id, int b_col_major, int M, int N, int K, const int8_t *A, int lda,
+                            const int8_t *B, int ldb, int32_t *C, int ldc, int blocks, hipStream_t stream) {
+    return persistent_entry(config_id, b_col_major ? 1 : 0, M, N, K, A, lda, B, ldb, C, ldc, blocks, stream);
 }
 
 int select_tile_config(int M, int N, int K) {

@@ -55,6 +55,16 @@ static const void *split_entry() {
         return nullptr;
 }
 
+// Persistent form of the whole-tile general kernel.
+template <class P, bool BCOL>
+static const void *persist_entry() {
+    if constexpr (P::family == 0)
+        return reinterpret_cast<const void *>(
+            &gemm_rc_persistent_kernel<P::mf, P::wm, P::wn, P::mt, P::nt, P::bk, stages_for<P, BCOL>(), !BCOL>);
+    else
+        return nullptr;
+}
+
 // The unpredicated general kernel for sizes that end inside a tile.
 template <class P, bool BCOL>
 static const void *edge_entry() {
@@ -127,6 +137,8 @@ void TDI8_CAT(register_cfg_, TDI8_CFG)(KernelSet *ks) {
     ks->kernel[0][1] = entry<P, false, true>();
     ks->kernel[1][0] = entry<P, true, false>();
     ks->kernel[1][1] = entry<P, true, true>();
+    ks->persist[0] = persist_entry<P, false>();
+    ks->persist[1] = persist_entry<P, true>();
     ks->prefetch = prefetch_entry<P>();
     ks->split[0] = split_entry<P, false>();
     ks->split[1] = split_entry<P, true>();

@@ -25,9 +25,11 @@ TDI8_CONFIG_LIST(TDI8_DEFINE_PARAMS)
 // inside a K tile (null for the skinny family); prefetch: the predicated
 // column-major-B kernel with the deep-prefetch K loop (null where the tile
 // does not fit it, and for the skinny family); conv: the implicit-GEMM
-// convolution form.
+// convolution form; persist[b_col_major]: the persistent form of the
+// whole-tile kernel (general family; null for the skinny family).
 struct KernelSet {
     const void *kernel[2][2];
+    const void *persist[2];
     const void *prefetch;
     const void *split[2];
     const void *edge[2];

@@ -74,9 +74,20 @@ constexpr int step_group(int ks, int f) {
 // EDGE: M, N or K may end inside a tile (chunks outside the operands read the
 // zero chunk, stores are masked); without it M, N and the K extent of a block
 // are whole tiles and the kernel carries none of these tests.
-template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW, bool SPLIT, bool EDGE, int SRC>
-__device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvParams &cv) {
+// PERSIST: the grid holds nblocks blocks (at most one tile each at a time);
+// block b computes tiles b, b + nblocks, b + 2 nblocks, ... of the same
+// XCD-grouped order (with nblocks a multiple of 8 a block stays on one XCD
+// and the blocks of an XCD keep walking one compact group of tiles).  Its
+// K tiles form one stream across tiles: the LDS refill of the last K tiles
+// of a tile already loads the next tile's first ones, and each finished
+// tile leaves straight from the accumulation registers (no LDS pass, no
+// barrier), so its stores drain while the matrix work of the next tile
+// runs.  Whole tiles only (M, N and K multiples of the tile), GEMM source.
+template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW, bool SPLIT, bool EDGE, int SRC,
+          bool PERSIST = false>
+__device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvParams &cv, int nblocks = 1) {
     static_assert(SRC == 0 || (!BROW && !SPLIT), "the convolution source is column-major B, unsplit");
+    static_assert(!PERSIST || (SRC == 0 && !SPLIT && !EDGE && MF == 32), "persistent form: whole tiles, GEMM");
     constexpr int NW = WM * WN;
     constexpr int BM = WM * MF * MT;
     constexpr int BN = WN * MF * NT;
@@ -96,6 +107,9 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
     constexpr int G = step_group(KS, MT * NT);   // K steps per operand group
     constexpr int KG = KS / G;                   // groups per K tile
     static_assert(KG % 2 == 0, "operand double buffer needs an even number of groups per tile");
+    // A load slot reads A or B for every wave alike (the persistent form
+    // shifts the two operands' pointers separately from tile to tile).
+    static_assert(!PERSIST || (A_CHUNKS / 64) % NW == 0, "load slots split A and B by slot index");
     constexpr int CPRB = BN / 16;                // 16-byte chunks per row-major B row
     static_assert(!BROW || (CPRB >= 4 && (BK * BN) % 1024 == 0), "row-major B form");
     using Acc = typename Mfma<MF>::Acc;
@@ -206,9 +220,19 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
         const bool is_b = (i * NW + wave) * 64 >= A_CHUNKS;
         return (BROW && is_b) ? static_cast<int64_t>(kt) * BK * g.ldb : static_cast<int64_t>(kt) * BK;
     };
+    // Persistent form: the load stream's position (K tile lt of the lj-th
+    // tile of this block) and the shifts of the A and B pointers from the
+    // first tile to that tile.
+    [[maybe_unused]] int lt = 0, lj = 0;
+    [[maybe_unused]] int64_t la = 0, lb = 0;
+    [[maybe_unused]] const int ptiles =
+        PERSIST ? (g.tiles_m * g.tiles_n - static_cast<int>(blockIdx.x) + nblocks - 1) / nblocks : 1;
     // Source of load slot i for K tile kt.
     auto source = [&](int i, int kt) -> const int8_t * {
-        if constexpr (SRC == 0 && EDGE) {
+        if constexpr (PERSIST) {
+            const bool is_a = i < A_CHUNKS / 64 / NW;
+            return src[i] + (is_a ? la : lb) + koff(i, lt);
+        } else if constexpr (SRC == 0 && EDGE) {
             return kt * BK < klim[i] ? src[i] + koff(i, kt) : zero_chunk;
         } else if constexpr (SRC == 0) {
             return src[i] + koff(i, kt);
@@ -255,6 +279,22 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
     auto issue = [&](int kt) {
 #pragma unroll
         for (int i = 0; i < LPW; ++i) issue_one(kt, i);
+    };
+    // Persistent form: the stream moves on by one K tile (all of its load
+    // slots issued); past a tile's last one it moves to the block's next
+    // tile.
+    auto advance = [&]() {
+        if constexpr (PERSIST) {
+            if (++lt == nk) {
+                lt = 0;
+                if (++lj < ptiles) {
+                    int tm2, tn2;
+                    tile_of_block(g, static_cast<int>(blockIdx.x) + lj * nblocks, tm2, tn2);
+                    la = static_cast<int64_t>(tm2 * BM - m0) * g.lda;
+                    lb = BROW ? static_cast<int64_t>(tn2 * BN - n0) : static_cast<int64_t>(tn2 * BN - n0) * g.ldb;
+                }
+            }
+        }
     };
 
     // LDS byte offsets (within a stage) of this lane's operand rows.
@@ -382,6 +422,7 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
                 // faster at 16384^2 x 8192, 7% slower with row-major B).
                 if constexpr (LOAD && BROW) {
                     issue(t + STAGES);
+                    advance();
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
@@ -399,6 +440,7 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                if constexpr (LOAD && !BROW) advance();
             }
             TDI8_WAIT_LGKM0();
             __builtin_amdgcn_sched_barrier(0);
@@ -406,6 +448,115 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
     };
     using T1 = std::true_type;
     using T0 = std::false_type;
+
+    if constexpr (PERSIST) {
+        // The tile's C straight from the accumulation registers, each store
+        // instruction writing whole 128-byte lines with the non-temporal
+        // hint.  Lane l = 32 h + r of an instruction tile holds, in its
+        // quads q = 0..3, row r's 16-byte pieces 2 q + h (columns
+        // 8 q + 4 h .. + 3).  Two lane exchanges regroup them: swapping
+        // 16-lane rows between quads 0/1 and 2/3 (v_permlane16_swap) puts
+        // rows 0..15 in quads 0 and 2 and rows 16..31 in quads 1 and 3, then
+        // swapping lanes 8 apart between quads 0/2 and 1/3 (DPP row_ror:8)
+        // leaves, for lane l = 32 h + 16 s + 8 t + k, row k (+8, +16, +24 in
+        // quads 2, 1, 3) piece 4 t + 2 s + h in every quad: one instruction
+        // per quad covers 8 rows x 128 bytes.
+        auto store_tile = [&](int j) {
+            int tm2, tn2;
+            tile_of_block(g, static_cast<int>(blockIdx.x) + j * nblocks, tm2, tn2);
+            const int k8 = lane & 7;
+            const bool t8 = (lane >> 3) & 1;
+            const int piece = 4 * (t8 ? 1 : 0) + 2 * ((lane >> 4) & 1) + (lane >> 5);
+            int32_t *cb = g.C + static_cast<int64_t>(tm2 * BM + wm * (MT * MF) + k8) * g.ldc + tn2 * BN +
+                          wn * (NT * MF) + 4 * piece;
+            constexpr int kRowOf[4] = {0, 16, 8, 24};  // first row held by quad 0, 1, 2, 3
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int jj = 0; jj < NT; ++jj) {
+                    int q[4][4];
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) q[qq][e] = acc[i][jj][4 * qq + e];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+                        for (int pq = 0; pq < 4; pq += 2) {
+                            const auto r = __builtin_amdgcn_permlane16_swap(q[pq][e], q[pq + 1][e], false, false);
+                            q[pq][e] = static_cast<int>(r[0]);
+                            q[pq + 1][e] = static_cast<int>(r[1]);
+                        }
+#pragma unroll
+                        for (int pq = 0; pq < 2; ++pq) {
+                            const int lo = __builtin_amdgcn_update_dpp(0, q[pq][e], 0x128, 0xf, 0xf, false);
+                            const int hi = __builtin_amdgcn_update_dpp(0, q[pq + 2][e], 0x128, 0xf, 0xf, false);
+                            q[pq][e] = t8 ? hi : q[pq][e];
+                            q[pq + 2][e] = t8 ? q[pq + 2][e] : lo;
+                        }
+                    }
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const i32x4 v = {q[qq][0], q[qq][1], q[qq][2], q[qq][3]};
+                        __builtin_nontemporal_store(
+                            v, reinterpret_cast<i32x4 *>(cb + static_cast<int64_t>(i * MF + kRowOf[qq]) * g.ldc + jj * MF));
+                    }
+                }
+        };
+        int ct = 0, cj = 0;  // K tile within the tile being computed, and that tile's index
+        // After each K tile of the stream: a tile whose last K tile is done
+        // is stored, and the accumulators start over for the next one.
+        auto finish = [&]() {
+            if (++ct == nk) {
+                ct = 0;
+                store_tile(cj++);
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) acc[i][j] = Acc{};
+            }
+        };
+        const int total = ptiles * nk;
+        if (total > 0) {
+            const int first = total < STAGES ? total : STAGES;
+            for (int s = 0; s < first; ++s) {
+                issue(s);
+                advance();
+            }
+            if (total >= STAGES) {
+                TDI8_WAIT_VMCNT((STAGES - 1) * LPW);
+            } else {
+                TDI8_WAIT_VMCNT(0);
+            }
+            block_barrier();
+            read_frags(0, 0, 0);
+            TDI8_WAIT_LGKM0();
+            __builtin_amdgcn_sched_barrier(0);
+            int u = 0;
+            for (; u + STAGES < total; ++u) {
+                tile(u, T1{}, T1{}, T1{});
+                finish();
+            }
+            if (u + STAGES == total && u + 1 < total) {
+                tile(u, T0{}, T1{}, T1{});
+                finish();
+                ++u;
+            }
+            for (; u + 1 < total; ++u) {
+                tile(u, T0{}, T1{}, T0{});
+                finish();
+            }
+            tile(u, T0{}, T0{}, T0{});
+            stamp.loop_done();
+            finish();
+        } else {
+            // K = 0: every tile of the block is zero.
+            stamp.loop_done();
+            for (int j = 0; j < ptiles; ++j) store_tile(j);
+        }
+        stamp.end(g);
+        return;
+    }
 
     if (nk > 0) {
         // Prologue: every buffer filled (tiles 0 .. STAGES-1), wait for tile 0.
@@ -553,6 +704,14 @@ __device__ __forceinline__ void pipelined_body(const GemmArgs &g, const ConvPara
 template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW, bool SPLIT, bool EDGE>
 __global__ void __launch_bounds__(WM * WN * 64) gemm_rc_pipelined_kernel(GemmArgs g) {
     pipelined_body<MF, WM, WN, MT, NT, BK, STAGES, BROW, SPLIT, EDGE, 0>(g, ConvParams{});
+}
+
+// Persistent form of the whole-tile kernel: nblocks blocks (at most the tile
+// count; a multiple of 8 keeps each block on one XCD) walk all tiles, see
+// PERSIST above.
+template <int MF, int WM, int WN, int MT, int NT, int BK, int STAGES, bool BROW>
+__global__ void __launch_bounds__(WM * WN * 64) gemm_rc_persistent_kernel(GemmArgs g, int nblocks) {
+    pipelined_body<MF, WM, WN, MT, NT, BK, STAGES, BROW, false, false, 0, true>(g, ConvParams{}, nblocks);
 }
 
 // Implicit-GEMM convolution ("先导杯比赛回顾", 卷积转化: the convolution
