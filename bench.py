@@ -456,15 +456,12 @@ def persistent_report(t, shapes=None):
     import torch
     torch.manual_seed(0)
     sh = torch.cuda.current_stream().cuda_stream
-    props = torch.cuda.get_device_properties(0)
-    print("| M×N×K | B | configuration | tiles | default µs (one block per tile) | persistent µs (blocks) | "
+    print("| M×N×K | B | configuration | tiles | default µs (one block per tile) | persistent µs | "
           "persistent / default |")
     print("|---|---|---|---|---|---|---|")
     for (M, N, K) in shapes or PERSIST_SHAPES:
         cfg = t.tile_config_info(t.select_tile_config(M, N, K))
         tiles = (M // cfg.block_m) * (N // cfg.block_n)
-        nb = props.multi_processor_count * max(cfg.blocks_per_cu, 1)
-        nb = min(nb - nb % 8 if nb >= 8 else nb, tiles)
         for bcm in (True, False):
             w = dict(M=M, N=N, K=K, bcm=bcm)
             nsets = rotation_sets(w)
@@ -504,7 +501,7 @@ def persistent_report(t, shapes=None):
                     res[name].append(e0.elapsed_time(e1) * 1e3 / reps)
             d = sorted(res["default"])[2]
             p = sorted(res["persistent"])[2]
-            print(f"| {M}×{N}×{K} | {'col' if bcm else 'row'} | {cfg.id} | {tiles} | {d:.1f} | {p:.1f} ({nb}) | "
+            print(f"| {M}×{N}×{K} | {'col' if bcm else 'row'} | {cfg.id} | {tiles} | {d:.1f} | {p:.1f} | "
                   f"{p / d:.3f} |", flush=True)
             del sets
             torch.cuda.empty_cache()

@@ -260,7 +260,7 @@ int gemm_plan(int config_id, int b_col_major, int M, int N, int K, const int8_t 
 
 /* Same product in the persistent form of a general configuration's
  * whole-tile kernel: `blocks` blocks (0: as many as the device holds at once,
- * the compute units times the configuration's resident blocks per unit,
+ * the compute units times the persistent kernel's resident blocks per unit,
  * rounded down to a multiple of 8; any value is capped at the tile count)
  * each walk the tiles blocks apart in the block-to-tile order of the other
  * forms, which groups the tiles resident on one XCD into a compact region

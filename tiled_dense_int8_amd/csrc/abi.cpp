@@ -78,6 +78,9 @@ struct DeviceState {
     int hip_error = 0;
     tdi8_hw_info hw{};
     int bpc[TDI8_NUM_CONFIGS] = {};
+    // resident blocks per compute unit of each persistent kernel [config][b_col_major]
+    // (its registers can differ from the one-tile-per-block kernel's)
+    int persist_bpc[TDI8_NUM_CONFIGS][2] = {};
 };
 
 DeviceState g_devices[kMaxDevices];
@@ -109,6 +112,17 @@ void init_device(DeviceState &ds, int dev) {
             return;
         }
         ds.bpc[id] = nb;
+        for (int b = 0; b < 2; ++b) {
+            const void *pk = kernels()[id].persist[b];
+            if (!pk) continue;
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, pk, c.threads, 0);
+            if (e != hipSuccess) {
+                ds.status = TDI8_ERR_HIP;
+                ds.hip_error = static_cast<int>(e);
+                return;
+            }
+            ds.persist_bpc[id][b] = nb;
+        }
     }
 }
 
@@ -310,7 +324,8 @@ int gemm_entry(int cfg, int bcol, int M, int N, int K, const int8_t *A, int lda,
 }
 
 // The persistent form of configuration id (general family) over whole tiles;
-// blocks 0 = one wave of resident blocks, rounded down to a multiple of 8.
+// blocks 0 = one wave of resident blocks of the persistent kernel itself (its
+// occupancy, not the one-tile kernel's), rounded down to a multiple of 8.
 int persistent_entry(int cfg, int bcol, int M, int N, int K, const int8_t *A, int lda, const int8_t *B, int ldb,
                      int32_t *C, int ldc, int blocks, hipStream_t stream) {
     int st = tdi8_validate(bcol, M, N, K, A, lda, B, ldb, C, ldc);
@@ -332,7 +347,8 @@ int persistent_entry(int cfg, int bcol, int M, int N, int K, const int8_t *A, in
     if (tiles > INT_MAX / c.threads) return TDI8_ERR_INVALID_VALUE;
     int64_t nb = blocks;
     if (nb == 0) {
-        nb = static_cast<int64_t>(ds->hw.num_cu) * (ds->bpc[id] > 0 ? ds->bpc[id] : 1);
+        const int pb = ds->persist_bpc[id][bcol ? 1 : 0];
+        nb = static_cast<int64_t>(ds->hw.num_cu) * (pb > 0 ? pb : 1);
         if (nb >= 8) nb -= nb % 8;
     }
     if (nb > tiles) nb = tiles;
