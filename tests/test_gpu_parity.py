@@ -569,8 +569,9 @@ def large_inputs_and_oracle():
 @pytest.mark.parametrize("bcm", [True, False])
 def test_workload_large_16384(lib, bcm):
     """Every element of the 16384 x 16384 x 8192 product against the oracle,
-    both B layouts, seed 0; C sits in a sentinel-filled buffer whose canary
-    after the last row must survive."""
+    both B layouts, seed 0, from the selected call and from the persistent
+    form; C sits in a sentinel-filled buffer whose canary after the last row
+    must survive."""
     M, N, K = 16384, 16384, 8192
     A, B, want = large_inputs_and_oracle()
     Bs = synthetic.store_b(B, bcm)
@@ -582,12 +583,22 @@ def test_workload_large_16384(lib, bcm):
     note(f"[case] cfg5 launch bcm={bcm} selected={lib.select_tile_config(M, N, K)}")
     lib.gemm(A_dev, B_dev, bcm, out=C_dev)
     torch.cuda.synchronize()
-    del A_dev, B_dev
     got = C_dev.cpu().numpy()
     if not np.array_equal(got, want):
         bad = np.argwhere(got != want)
         raise AssertionError(f"cfg5 bcm={bcm}: {len(bad)} mismatches, first at {tuple(bad[0])}")
     assert (C_buf[M * N:].cpu().numpy() == -123456789).all(), "wrote past C"
+    # the persistent form of the same configuration: 16 tiles per block
+    note(f"[case] cfg5 persistent launch bcm={bcm}")
+    C_buf.fill_(-123456789)
+    lib.gemm(A_dev, B_dev, bcm, out=C_dev, persistent_blocks=0)
+    torch.cuda.synchronize()
+    del A_dev, B_dev
+    got = C_dev.cpu().numpy()
+    if not np.array_equal(got, want):
+        bad = np.argwhere(got != want)
+        raise AssertionError(f"cfg5 persistent bcm={bcm}: {len(bad)} mismatches, first at {tuple(bad[0])}")
+    assert (C_buf[M * N:].cpu().numpy() == -123456789).all(), "persistent form wrote past C"
     del got, C_buf, C_dev
     torch.cuda.empty_cache()
 
