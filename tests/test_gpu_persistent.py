@@ -96,3 +96,26 @@ def test_persistent_workload_4096(lib, bcm):
         note(f"[case] persistent 4096^3 bcm={bcm} blocks={blocks}")
         case.c_buf.fill_(-123456789)
         check_case(case, f"persistent 4096^3 blocks={blocks}", persistent=blocks, expect=want)
+
+
+@pytest.mark.parametrize("bcm", [True, False])
+def test_persistent_random_cases(lib, bcm):
+    """Seeded random whole-tile shapes for random general configurations:
+    random tile counts along M and N, K tile counts from 1 to 9, block counts
+    from 1 to past the tile count, leading dimensions padded by multiples of
+    16 (ldc by multiples of 4) and operands offset by multiples of 16 bytes."""
+    t = lib
+    cfgs = general(t)
+    rng = np.random.default_rng(20261203 + (1 if bcm else 0))
+    for i in range(48):
+        c = cfgs[int(rng.integers(0, len(cfgs)))]
+        tm, tn, tk = (int(rng.integers(1, 5)), int(rng.integers(1, 5)), int(rng.integers(1, 10)))
+        M, N, K = tm * c.block_m, tn * c.block_n, tk * c.block_k
+        blocks = int(rng.integers(0, tm * tn + 3))
+        lda = K + 16 * int(rng.integers(0, 3))
+        ldb = (K if bcm else N) + 16 * int(rng.integers(0, 3))
+        ldc = N + 4 * int(rng.integers(0, 3))
+        offs = (16 * int(rng.integers(0, 2)), 16 * int(rng.integers(0, 2)), 4 * int(rng.integers(0, 2)))
+        A, B = synthetic.gemm_inputs(M, N, K, seed=5000 + i)
+        case = DeviceCase(A, B, bcm, lda=lda, ldb=ldb, ldc=ldc, offsets=offs)
+        check_case(case, f"persistent random {i} config {c.id} blocks={blocks}", config=c.id, persistent=blocks)
