@@ -230,8 +230,9 @@ typedef enum {
     TDI8_FORM_SKINNY_ROW_GROUPS = 8,/* zero fill, then the row-major-B column groups of a skinny tile */
     TDI8_FORM_PREDICATED_PREFETCH = 9, /* the predicated kernel with two K tiles of loads in flight:
                                        * column-major B, at most one block per compute unit */
-    TDI8_FORM_PERSISTENT = 10       /* persistent whole-tile kernel: a fixed grid walks the tiles
-                                       (gemm_s8s8s32_persistent) */
+    TDI8_FORM_PERSISTENT = 10       /* persistent whole-tile kernel: a fixed grid walks the tiles;
+                                       run only by gemm_s8s8s32_persistent, so gemm_plan, which
+                                       describes the other gemm calls, never reports it */
 } tdi8_form;
 
 typedef struct {
