@@ -119,3 +119,37 @@ def test_persistent_random_cases(lib, bcm):
         A, B = synthetic.gemm_inputs(M, N, K, seed=5000 + i)
         case = DeviceCase(A, B, bcm, lda=lda, ldb=ldb, ldc=ldc, offsets=offs)
         check_case(case, f"persistent random {i} config {c.id} blocks={blocks}", config=c.id, persistent=blocks)
+
+
+def test_persistent_graph_capture_and_replay(lib):
+    """The persistent entry point only enqueues its kernel, so a call can be
+    captured into a HIP graph; every replay, with eager work in between,
+    reproduces the oracle's bytes (two tiles per block)."""
+    import oracle
+    t = lib
+    c = t.tile_config_info(0)
+    M, N, K = 2 * c.block_m, 2 * c.block_n, 4 * c.block_k
+    A, B = synthetic.gemm_inputs(M, N, K, seed=9)
+    want = oracle.gemm(A, B, False)
+    for bcm in (True, False):
+        note(f"[case] persistent graph capture {M}x{N}x{K} bcm={bcm}")
+        Ad = torch.from_numpy(A).cuda()
+        Bd = torch.from_numpy(synthetic.store_b(B, bcm)).cuda()
+        out = torch.empty((M, N), dtype=torch.int32, device="cuda")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            t.gemm(Ad, Bd, bcm, out=out, config=0, persistent_blocks=2)   # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            t.gemm(Ad, Bd, bcm, out=out, config=0, persistent_blocks=2)
+        for r in range(4):
+            out.fill_(-7)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), want), f"replay {r}"
+            t.gemm(Ad, Bd, bcm)                   # eager work between replays
+            torch.cuda.synchronize()
